@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the entry module's smoke
+check and the benchmark's CPU-baseline leg, never by the product path.
+"""
+from .attention import allowed_mask, attention_fp64, softmax_rows_fp64
+
+__all__ = ["allowed_mask", "attention_fp64", "softmax_rows_fp64"]

@@ -1,0 +1,122 @@
+"""Reference (oracle) implementation of scaled dot-product attention, fp64, CPU.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import this module:
+only the tests, the smoke check of the entry module and the CPU-baseline leg of
+the benchmark call it.  It shares no code with the HIP library and imports
+nothing from the package.
+
+What it computes (the plain definition; the fused GPU kernel reaches the same
+value by reassociating the sums):
+
+    Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V
+
+  * formula: "Attention Is All You Need" overview (azimuth.plus), section "The
+    idea: every word queries every word"; the LaTeX form in the notebook
+    chapter (antoniofranca.me), section "Multi-Head Self-Attention"; the
+    cuijiawei.cn summary, section "The core idea: scaled dot-product attention".
+  * the scores are divided by sqrt(d_k) (aiany.app explainer, Step 5 "Scale:
+    divide by 8" and Step 6 matrix form S = QK^T / sqrt(dk); the division sign
+    is lost in that page's one-line formula, every other statement has it).
+    Here the caller passes the scale explicitly, normally 1/sqrt(d_k).
+  * softmax is taken per query row, after subtracting the row maximum (the
+    overview page's NumPy snippet, "stable softmax"); every row of weights sums
+    to one (aiany.app Step 6, A = softmax(S), "each row sums to 1").
+  * masked scores are -inf before the softmax, so their weight is exactly 0:
+    causal rule e_tj = -inf for j > t (notebook chapter, section "Masked
+    Attention in the Decoder"); generic mask `masked_fill(mask == 0, -inf)`
+    (cuijiawei.cn, section "Minimal PyTorch implementation").  Key padding is
+    read as that generic mask with mask[b, :, :, j] = (j < L_b).
+  * output row = weighted sum of the value rows (aiany.app Step 5, "Weigh each
+    value" / "Sum -- and you have z1"; Step 6, Z = AV).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * causal with Tq != Tk: the literal rule j <= i (top-left aligned).
+  * a row with no allowed key (L_b = 0, or Tk = 0) outputs zeros.
+  * key lengths outside [0, Tk] are clamped to that range.
+
+The softmax is deliberately the two-pass form (max, then exp / sum), not the
+running (online) form the kernel uses, so agreement between the two pins the
+kernel's rescaling.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["allowed_mask", "attention_fp64", "softmax_rows_fp64"]
+
+
+def allowed_mask(rows: np.ndarray, Tk: int, causal: bool, key_len: int | None) -> np.ndarray:
+    """Boolean [len(rows), Tk]: True where query row `rows[i]` may attend key j.
+
+    Key j is allowed iff (not causal or j <= row) and (no key length or j < L),
+    with L clamped to [0, Tk] (causal rule: notebook chapter, "Masked Attention
+    in the Decoder"; padding as the generic mask of the cuijiawei.cn snippet).
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    j = np.arange(Tk, dtype=np.int64)[None, :]
+    ok = np.ones((rows.shape[0], Tk), dtype=bool)
+    if causal:
+        ok &= j <= rows[:, None]
+    if key_len is not None:
+        L = min(max(int(key_len), 0), Tk)
+        ok &= j < L
+    return ok
+
+
+def softmax_rows_fp64(scores: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """Row softmax of fp64 `scores` restricted to `allowed`; masked weights are 0.
+
+    Two passes: row max over allowed entries, then exp(s - max) / sum (the
+    overview page's stable softmax).  A row with no allowed entry gets all-zero
+    weights.
+    """
+    s = np.where(allowed, scores, -np.inf)
+    any_ok = allowed.any(axis=-1, keepdims=True)
+    m = np.where(any_ok, s.max(axis=-1, keepdims=True, initial=-np.inf), 0.0)
+    e = np.exp(s - m)  # exp(-inf) = 0 for masked entries
+    z = e.sum(axis=-1, keepdims=True)
+    return np.where(any_ok, e / np.where(any_ok, z, 1.0), 0.0)
+
+
+def attention_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None,
+                   rows=None, heads=None, return_weights: bool = False, block: int = 256):
+    """Scaled dot-product attention in fp64 for [B, h, T, d] inputs.
+
+    q: [B, h, Tq, d_k], k: [B, h, Tk, d_k], v: [B, h, Tk, d_v]; any real dtype,
+    widened exactly to fp64 (pass the values the GPU sees, e.g. bf16-rounded).
+    scale: the score multiplier (normally 1/sqrt(d_k)), used as given.
+    key_lens: None or int sequence [B] (valid key count per batch entry).
+    rows: None (all query rows) or a 1-D index array: only those rows are
+      computed, for every (b, head) selected.
+    heads: None (all) or a list of (b, head) pairs to compute; others are left 0.
+    Returns out [B, h, R, d_v] fp64 (R = Tq or len(rows)) and, when
+    return_weights, the weights [B, h, R, Tk].
+    Processes each (b, head) in blocks of `block` query rows so the score
+    matrix is never held whole.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, Tq, dk = q.shape
+    Tk = k.shape[2]
+    dv = v.shape[3]
+    assert k.shape == (B, H, Tk, dk) and v.shape == (B, H, Tk, dv)
+    row_idx = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = row_idx.shape[0]
+    out = np.zeros((B, H, R, dv), dtype=np.float64)
+    wts = np.zeros((B, H, R, Tk), dtype=np.float64) if return_weights else None
+    pairs = [(b, hh) for b in range(B) for hh in range(H)] if heads is None else list(heads)
+    sc = float(scale)
+    for b, hh in pairs:
+        L = None if key_lens is None else int(np.asarray(key_lens)[b])
+        kb = k[b, hh].astype(np.float64)
+        vb = v[b, hh].astype(np.float64)
+        for r0 in range(0, R, block):
+            ridx = row_idx[r0:r0 + block]
+            qb = q[b, hh, ridx].astype(np.float64)
+            s = (qb @ kb.T) * sc
+            w = softmax_rows_fp64(s, allowed_mask(ridx, Tk, causal, L))
+            out[b, hh, r0:r0 + block] = w @ vb
+            if return_weights:
+                wts[b, hh, r0:r0 + block] = w
+    return (out, wts) if return_weights else out
