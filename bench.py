@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one attn_fwd launch over the whole workload (default: B1 h16
+Tq=Tk=16384 d128 bf16, unmasked: the non-causal long-sequence case the
+throughput target is quoted on).  Inputs are generated once, seeded, and are
+resident in device memory before the timed region.  Prints ONE JSON line:
+
+  value      attention TFLOP/s, 4*B*h*Tq*Tk*d flops per step (halved for causal)
+  roofline   matrix-core roofline of the kernel: achieved TFLOP/s from HIP
+             events on the launch stream vs the 2.5 PFLOP/s dense-bf16 peak;
+             traffic = HBM bytes per launch from the committed rocprofv3
+             counter summary when it matches the current kernel source
+  hbm        compulsory bytes (read Q, K, V once, write O once) / time vs 8 TB/s
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
+             workload on this host's cores (reported, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of MFMA bf16 peak (B*h*T^2*d shapes), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix/vector peak (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_t or m_d.group(1) != digest:
+        return None
+    return float(m_t.group(1))
+
+
+def flops_per_step(w) -> float:
+    f = 4.0 * w.B * w.h * w.Tq * w.Tk * w.d
+    return f / 2 if w.causal else f
+
+
+def compulsory_bytes(w) -> float:
+    es = 2 if w.dtype == "bf16" else 4
+    return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
+
+
+def cpu_baseline(w, q, k, v, key_lens, budget_s: float):
+    """fp64 oracle on a bounded sample: blocks of 256 query rows (seeded order),
+    all heads, until `budget_s` of CPU time is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention_fp64
+
+    cores = len(os.sched_getaffinity(0))
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    kl = None if key_lens is None else key_lens.numpy()
+    order = np.random.default_rng(0).permutation(w.Tq)  # every row, seeded order
+    done_rows = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while done_rows < w.Tq:
+            rows = np.sort(order[done_rows:done_rows + 256])
+            attention_fp64(qn, kn, vn, w.scale, causal=w.causal, key_lens=kl, rows=rows)
+            done_rows += rows.shape[0]
+            if w.causal:
+                kk = np.minimum(rows + 1, w.Tk).sum()
+            else:
+                kk = rows.shape[0] * w.Tk
+            flops += 4.0 * w.B * w.h * float(kk) * w.d
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{done_rows} of {w.Tq} query rows (blocks of 256, seeded order) x "
+                   f"{w.B * w.h} heads, fp64 NumPy/OpenBLAS, {el:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (--gpus 1); multi-GPU runs are not "
+              "supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_scaled_dot_03_amd as tsd
+    from transformer_scaled_dot_03_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    tsd.raw_library()  # loud failure if the HIP library is missing
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, kl = make_inputs(w, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    kld = None if kl is None else kl.to(dev)
+    out = torch.empty((w.B, w.h, w.Tq, w.d), dtype=qd.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    fn = tsd.attn_fwd if w.dtype == "bf16" else tsd.attn_fwd_f32
+    mask = (tsd.MASK_CAUSAL if w.causal else 0) | (tsd.MASK_KEYPAD if w.keypad else 0)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr())
+    klp = None if kld is None else kld.data_ptr()
+    st = stream.cuda_stream
+
+    def step():
+        rc = fn(*ptrs, w.B, w.h, w.Tq, w.Tk, w.d, w.d, w.scale, mask, klp, st)
+        if rc != tsd.OK:
+            raise RuntimeError(f"attn_fwd failed: {tsd.attn_status_str(rc)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps       # average per launch, HIP events
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copy calibration: {nbytes} bytes read + {nbytes} bytes written per copy kernel",
+              file=sys.stderr)
+
+    ms_per_step = wall * 1e3 / args.steps
+    fl = flops_per_step(w)
+    value = fl / (ms_per_step * 1e-3) / 1e12
+    achieved = fl / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    digest = kernel_source_digest()
+    traffic = committed_traffic(name, digest)
+    cb = compulsory_bytes(w)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, recipe in workloads.py)",
+        "config": {"workload": name, "B": w.B, "h": w.h, "Tq": w.Tq, "Tk": w.Tk, "d": w.d,
+                   "causal": w.causal, "key_padding": w.keypad, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_ms": round(ev_ms, 4), "kernel_source_digest": digest},
+        "hbm": {"compulsory_bytes": cb, "achieved_GBs": round(cb / (ev_ms * 1e-3) / 1e9, 1),
+                "peak_GBs": PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

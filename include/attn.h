@@ -1,0 +1,120 @@
+/*
+ * attn.h -- C ABI of libattn.so: fused scaled dot-product attention forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Operation (per batch entry b and head, for every query row i):
+ *
+ *     out[b,h,i,:] = sum_j w_ij * v[b,h,j,:],
+ *     w_ij = exp(s_ij - m_i) / sum_{j' allowed} exp(s_ij' - m_i),
+ *     s_ij = scale * <q[b,h,i,:], k[b,h,j,:]>,  m_i = max over allowed j of s_ij,
+ *
+ * i.e. Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k)) V as defined in
+ * "Attention Is All You Need" (overview on azimuth.plus, section "The idea:
+ * every word queries every word"; notebook chapter on antoniofranca.me,
+ * section "Multi-Head Self-Attention"; cuijiawei.cn, section "The core idea:
+ * scaled dot-product attention"), with the caller supplying the scale
+ * (normally 1/sqrt(d_k): aiany.app explainer, Step 5 "Scale: divide by 8").
+ * Heads are independent (multi-head layout [B, h, T, d] of the cuijiawei.cn
+ * MultiHeadAttention snippet).  Weights for disallowed keys are exactly 0:
+ *
+ *   ATTN_MASK_CAUSAL: key j is allowed for query row i only if j <= i
+ *     (notebook chapter, "Masked Attention in the Decoder", the e_tj cases),
+ *     applied literally (top-left aligned) also when Tq != Tk.
+ *   ATTN_MASK_KEYPAD: key j of batch entry b is allowed only if j < L_b,
+ *     L_b = key_lens[b] clamped to [0, Tk] (the generic masked_fill(mask == 0,
+ *     -inf) of the cuijiawei.cn snippet with a per-sequence length mask).
+ *   Both bits may be set: the allowed set is the intersection.
+ *   A query row with no allowed key (L_b = 0, or Tk = 0) gets an all-zero output.
+ *
+ * Layout: all tensors dense, row-major, no strides:
+ *   q   [B, h, Tq, d_k]     k [B, h, Tk, d_k]     v [B, h, Tk, d_v]
+ *   out [B, h, Tq, d_v]     key_lens int32 [B] (device memory), or NULL
+ * Offsets are computed in 64-bit arithmetic.
+ *
+ * Ownership: every pointer is caller-owned device memory (HIP / PyTorch
+ * allocations); the library allocates nothing and keeps no per-call state.
+ *
+ * Asynchrony: the work is enqueued on `stream` (0 = the null stream) and the
+ * call returns without synchronising.  key_lens is read by the kernel, so its
+ * values are never validated on the host; they are clamped to [0, Tk].
+ *
+ * Errors: 0 on success.  Argument errors return a negative ATTN_ERR_* code
+ * before any HIP call is made (nothing is launched); a failed launch returns
+ * ATTN_ERR_HIP and the hipError_t is kept per thread (attn_last_hip_error).
+ * The library never prints and never aborts.
+ *
+ * Empty work: B, h or Tq equal to 0 is a valid no-op (pointers unused).
+ * Tk = 0 is valid: every output row is written as zeros (k, v unused).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* bits of mask_kind (bitwise OR) */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_KEYPAD = 2
+};
+
+/* status codes */
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,        /* a pointer that must be non-NULL is NULL */
+  ATTN_ERR_SHAPE = -2,       /* negative dimension, or d_k != d_v */
+  ATTN_ERR_HEADDIM = -3,     /* head size not supported (supported: 64, 128) */
+  ATTN_ERR_MASK = -4,        /* unknown mask bits, or KEYPAD with key_lens == NULL */
+  ATTN_ERR_ALIAS = -5,       /* out overlaps q, k or v */
+  ATTN_ERR_ALIGN = -6,       /* q, k, v or out not 16-byte aligned; key_lens not 4-byte aligned */
+  ATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
+  ATTN_ERR_TOO_LARGE = -8,   /* B*h*ceil(Tq/128) work-groups exceed the launch limit */
+  ATTN_ERR_HIP = -100        /* the kernel launch failed; see attn_last_hip_error() */
+};
+
+/*
+ * attn_fwd: bfloat16 q, k, v and out; fp32 accumulation and fp32 softmax
+ * state; the probabilities are rounded to bfloat16 (round-to-nearest-even)
+ * before the probability-value product, and the output is rounded once to
+ * bfloat16 (round-to-nearest-even).
+ *   q, k, v, out : device pointers, bfloat16 elements, layout above
+ *   B, h         : batch entries and heads (>= 0)
+ *   Tq, Tk       : query and key/value lengths (>= 0)
+ *   d_k, d_v     : head sizes; must be equal, 64 or 128
+ *   scale        : finite score multiplier (any sign; 0 gives uniform weights)
+ *   mask_kind    : OR of ATTN_MASK_* bits
+ *   key_lens     : device int32 [B] when ATTN_MASK_KEYPAD is set, else ignored
+ *   stream       : HIP stream the kernel is enqueued on
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out,
+             int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
+             int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
+ * attn_fwd_f32: identical parameter list and semantics with fp32 q, k, v and
+ * out; every product, sum and the softmax are computed in fp32 (no bfloat16
+ * rounding anywhere).
+ */
+int attn_fwd_f32(const void* q, const void* k, const void* v, void* out,
+                 int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
+                 int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+/* The hipError_t of the last failed launch on the calling thread (0 if none). */
+int attn_last_hip_error(void);
+
+/* Library version string, e.g. "attn 0.1.0 gfx950". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/attn.h declares, and
+reject bad arguments with the documented status before any HIP call (the
+pointers below are never dereferenced; these calls make no HIP call at all).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from transformer_scaled_dot_03_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from transformer_scaled_dot_03_amd import build
+        build.build()
+    return _lib
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+
+
+def _declared_enum():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return {k: int(v) for k, v in re.findall(r"\b(ATTN_\w+)\s*=\s*(-?\d+)", src)}
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(
+        ["attn_fwd", "attn_fwd_f32", "attn_status_str", "attn_last_hip_error", "attn_version"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.raw_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    # and the binding covers exactly the declared set
+    assert sorted(L.SIGNATURES) == _declared_functions()
+
+
+def test_status_constants_match_header(L):
+    enum = _declared_enum()
+    assert enum["ATTN_OK"] == L.OK
+    for name in ("NULL", "SHAPE", "HEADDIM", "MASK", "ALIAS", "ALIGN", "SCALE", "TOO_LARGE", "HIP"):
+        assert enum["ATTN_ERR_" + name] == getattr(L, "ERR_" + name)
+    for name in ("NONE", "CAUSAL", "KEYPAD"):
+        assert enum["ATTN_MASK_" + name] == getattr(L, "MASK_" + name)
+
+
+def test_status_strings_and_version(L):
+    for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_HEADDIM, L.ERR_MASK, L.ERR_ALIAS,
+                 L.ERR_ALIGN, L.ERR_SCALE, L.ERR_TOO_LARGE, L.ERR_HIP):
+        s = L.attn_status_str(code)
+        assert s and s != "unknown status"
+    assert L.attn_status_str(12345) == "unknown status"
+    assert "gfx950" in L.attn_version()
+    assert L.attn_last_hip_error() == 0
+
+
+# fake, well-aligned, non-overlapping device addresses: never dereferenced
+Q, K, V, O, KL = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(q=Q, k=K, v=V, out=O, B=2, h=3, Tq=70, Tk=90, d_k=64, d_v=64, scale=0.125,
+            mask_kind=0, key_lens=None, stream=None)
+
+
+def _call(L, f32=False, **over):
+    a = dict(GOOD)
+    a.update(over)
+    fn = L.attn_fwd_f32 if f32 else L.attn_fwd
+    return fn(a["q"], a["k"], a["v"], a["out"], a["B"], a["h"], a["Tq"], a["Tk"], a["d_k"],
+              a["d_v"], a["scale"], a["mask_kind"], a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("f32", [False, True])
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "ERR_SHAPE"),
+    (dict(h=-2), "ERR_SHAPE"),
+    (dict(Tq=-1), "ERR_SHAPE"),
+    (dict(Tk=-1), "ERR_SHAPE"),
+    (dict(d_v=128), "ERR_SHAPE"),
+    (dict(d_k=32, d_v=32), "ERR_HEADDIM"),
+    (dict(d_k=256, d_v=256), "ERR_HEADDIM"),
+    (dict(d_k=0, d_v=0), "ERR_HEADDIM"),
+    (dict(mask_kind=4), "ERR_MASK"),
+    (dict(mask_kind=-1), "ERR_MASK"),
+    (dict(mask_kind=2), "ERR_MASK"),            # key padding without key_lens
+    (dict(mask_kind=3), "ERR_MASK"),
+    (dict(scale=float("nan")), "ERR_SCALE"),
+    (dict(scale=float("inf")), "ERR_SCALE"),
+    (dict(scale=-math.inf), "ERR_SCALE"),
+    (dict(q=None), "ERR_NULL"),
+    (dict(out=None), "ERR_NULL"),
+    (dict(k=None), "ERR_NULL"),
+    (dict(v=None), "ERR_NULL"),
+    (dict(q=Q + 8), "ERR_ALIGN"),
+    (dict(k=K + 2), "ERR_ALIGN"),
+    (dict(v=V + 4), "ERR_ALIGN"),
+    (dict(out=O + 12), "ERR_ALIGN"),
+    (dict(mask_kind=2, key_lens=KL + 2), "ERR_ALIGN"),
+    (dict(out=Q), "ERR_ALIAS"),
+    (dict(out=K + 4096), "ERR_ALIAS"),
+    (dict(out=V - 16), "ERR_ALIAS"),
+    (dict(B=1 << 30, h=1 << 10, Tq=1 << 20), "ERR_TOO_LARGE"),
+])
+def test_bad_arguments_rejected_before_any_launch(L, f32, over, code):
+    assert _call(L, f32=f32, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(h=0), dict(Tq=0), dict(B=0, q=None, out=None),
+                                  dict(Tq=0, q=None, k=None, v=None, out=None)])
+def test_empty_problem_is_a_no_op(L, over):
+    assert _call(L, **over) == L.OK
+
+
+def test_keypad_needs_key_lens_even_when_empty(L):
+    assert _call(L, B=0, mask_kind=L.MASK_KEYPAD) == L.ERR_MASK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from transformer_scaled_dot_03_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.LibraryMissing):
+        _lib.attn_version()

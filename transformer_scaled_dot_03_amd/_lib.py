@@ -1,0 +1,92 @@
+"""ctypes binding of libattn.so: argument marshalling only.
+
+Every function here forwards to the C ABI declared in include/attn.h with the
+same name and parameter list; all computation happens in the HIP kernels.
+If the library has not been built the import fails loudly: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEYPAD = 2
+
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_HEADDIM = -3
+ERR_MASK = -4
+ERR_ALIAS = -5
+ERR_ALIGN = -6
+ERR_SCALE = -7
+ERR_TOO_LARGE = -8
+ERR_HIP = -100
+
+# names and C signatures of every exported entry point (kept in step with attn.h)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_FWD_ARGS = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P]
+SIGNATURES = {
+    "attn_fwd": (_I, _FWD_ARGS),
+    "attn_fwd_f32": (_I, _FWD_ARGS),
+    "attn_status_str": (ctypes.c_char_p, [_I]),
+    "attn_last_hip_error": (_I, []),
+    "attn_version": (ctypes.c_char_p, []),
+}
+
+
+class LibraryMissing(ImportError):
+    pass
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise LibraryMissing(
+            f"{LIB_PATH} is not built: run `python -m transformer_scaled_dot_03_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = None
+
+
+def raw_library():
+    """The loaded ctypes.CDLL; loaded on first use, raises LibraryMissing if unbuilt."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def attn_fwd(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream) -> int:
+    """bf16 attention forward (attn.h `attn_fwd`); pointers are ints (device addresses)."""
+    return raw_library().attn_fwd(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream)
+
+
+def attn_fwd_f32(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream) -> int:
+    """fp32 attention forward (attn.h `attn_fwd_f32`)."""
+    return raw_library().attn_fwd_f32(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+                                      stream)
+
+
+def attn_status_str(status: int) -> str:
+    return raw_library().attn_status_str(status).decode()
+
+
+def attn_last_hip_error() -> int:
+    return raw_library().attn_last_hip_error()
+
+
+def attn_version() -> str:
+    return raw_library().attn_version().decode()

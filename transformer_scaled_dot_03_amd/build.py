@@ -1,0 +1,65 @@
+"""Build libattn.so (the HIP kernels + C ABI) in-tree with hipcc for gfx950.
+
+    python -m transformer_scaled_dot_03_amd.build
+
+The library is written next to this file; the Python binding loads it from
+there.  Build happens on any host with ROCm (no GPU needed: hipcc
+cross-compiles for gfx950).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libattn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["attn_fwd_kernel.hip", "attn_api.hip"]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code (kept out on
+# purpose; hipcc's host pass warns that it does not know the feature).
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: ROCm is required to build libattn.so")
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile every source into LIB_PATH (always recompiles); return the path."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    fd, tmp = tempfile.mkstemp(prefix=".libattn.", suffix=".so.tmp", dir=PKG)
+    os.close(fd)
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+    try:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (res.returncode, " ".join(cmd), res.stderr))
+        if verbose:
+            noise = "is not a recognized feature for this target"
+            msg = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+            if msg.strip():
+                print(msg, file=sys.stderr)
+        os.replace(tmp, LIB_PATH)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,516 @@
+// Fused scaled dot-product attention forward for gfx950 (MI355X).
+//
+//   O = softmax(scale * Q K^T) V   per (batch, head), optional causal and
+//   key-padding masks ("Attention Is All You Need": overview page, section
+//   "The idea: every word queries every word"; notebook chapter, sections
+//   "Multi-Head Self-Attention" and "Masked Attention in the Decoder").
+//
+// One work-group (4 waves, 256 threads) owns BM = 128 query rows of one
+// (b, head); wave w owns rows [32w, 32w + 32).  The key/value sequence is
+// streamed in tiles of BN keys through LDS (double-buffered: the global loads
+// of tile t+1 are in flight while tile t is computed).  The softmax is the
+// running (online) form: per row a running maximum m and sum l, with the
+// output accumulator rescaled by exp2(m_old - m_new) whenever m grows
+// (Milakov & Gimelshein 2018, "Online normalizer calculation for softmax";
+// the pages only name the fused FlashAttention family).  The score matrix is
+// never written to memory.
+//
+// Matrix-core mapping (bf16 path, v_mfma_f32_32x32x16_bf16, 64-lane wave,
+// lane l, g = l / 32, c = l % 32):
+//   * S^T = K Q^T: the A operand is a 32-key slice of K from LDS, the B
+//     operand is the wave's Q rows held in registers.  The accumulator then
+//     holds, in lane l, query row c and 16 of the 32 keys; lane l ^ 32 holds
+//     the other 16 keys of the same row.  Row max and row sum therefore need a
+//     single exchange between the two lane halves.
+//   * The K rows are fed in the order sigma (bits 2 and 3 of the key slot
+//     swapped), so accumulator registers 8m .. 8m+7 of a lane hold 8
+//     consecutive keys 16m + 8g + (0..7).  Those 8 probabilities are exactly
+//     the B operand of O^T = V^T P^T for keys 16m .. 16m+15: no data movement
+//     between the two products.
+//   * V is stored transposed in LDS (Vt[dv][key]) while staging, so the A
+//     operand of the second product is one 16-byte LDS read per lane.
+//   * The output accumulator O^T holds, in lane l, row c and d/2 contiguous
+//     output columns (dv permuted by tau), so the epilogue writes d bytes of
+//     contiguous bf16 per lane.
+// The fp32 path uses v_mfma_f32_32x32x2_f32 with the same S^T form; its PV
+// product takes one key per lane per step, so V needs no transpose there.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per work-group
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+// Work-group id -> (b*h + head, query tile).  The hardware hands consecutive
+// work-group ids to the 8 XCDs in turn; remap so each XCD receives a
+// contiguous range of logical ids, i.e. all query tiles of a (b, head) land on
+// the same XCD and share K/V through its L2.  Causal tiles run longest first.
+__device__ __forceinline__ void tile_of_block(int n_qtiles, bool causal, int& bh, int& qt) {
+  const int pid = blockIdx.x;
+  const int G = gridDim.x;
+  const int xcd = pid % kXcds, idx = pid / kXcds;
+  const int per = G / kXcds, rem = G % kXcds;
+  const int wg = (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+  bh = wg / n_qtiles;
+  qt = wg - bh * n_qtiles;
+  if (causal) qt = n_qtiles - 1 - qt;
+}
+
+__device__ __forceinline__ int clamp_len(const int32_t* key_lens, int b, int Tk) {
+  int L = key_lens[b];
+  return L < 0 ? 0 : (L > Tk ? Tk : L);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernel
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool KEYPAD>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
+  constexpr int BN = 64;                 // keys per tile
+  constexpr int KSTR = D + 8;            // K row stride in LDS (elements): +16 B pad
+  constexpr int VSTR = BN + 8;           // Vt row stride in LDS (elements): +16 B pad
+  constexpr int K_ELEMS = BN * KSTR;
+  constexpr int V_ELEMS = D * VSTR;
+  constexpr int BUF = K_ELEMS + V_ELEMS;
+  constexpr int DT = D / 16;             // MFMA steps over d for S^T
+  constexpr int NO = D / 32;             // 32-column tiles of the output
+  constexpr int NK = BN * D / 8 / kThreads;   // 16-byte K chunks per thread
+  constexpr int KG = BN * D / 8 / kThreads;   // keys per thread in the V transpose
+  constexpr int NA = BN / KG;                 // key groups per tile
+  static_assert(KG == 2 || KG == 4, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+
+  int bh, qt;
+  tile_of_block(p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int q0 = qt * kBM;
+  const int qw = q0 + 32 * w;          // first row of this wave
+  const int row = qw + c;              // this lane's query row
+
+  int kend = Tk;                       // keys [0, kend) hold data
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  int kend_wg = kend;
+  if (CAUSAL) kend_wg = min(kend_wg, q0 + kBM);
+  const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
+  int kend_w = CAUSAL ? min(kend, qw + 32) : kend;
+  if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
+  const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
+
+  const __bf16* Qg = static_cast<const __bf16*>(p.q) + (int64_t)bh * Tq * D;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + (int64_t)bh * Tk * D;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + (int64_t)bh * Tk * D;
+  __bf16* Og = static_cast<__bf16*>(p.o) + (int64_t)bh * Tq * D;
+
+  // Q rows -> registers (B operand of S^T); d index of step t is 16t + 8g + e.
+  bf16x8 qf[DT];
+  {
+    const bool ok = row < Tq;
+    const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * D + 8 * g;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+      if (p.neg) x ^= 0x80008000u;     // negative scale: use -Q and |scale| (exact)
+      qf[t] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  // staging registers for one K/V tile
+  u32x4 kreg[NK];
+  u32x4 vreg[KG];
+  const int va = tid % NA, vc = tid / NA;   // V unit: keys KG*va .., columns 8vc ..
+
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int ch = tid + kThreads * u;
+      const int kr = ch / (D / 8), kc = ch % (D / 8);
+      const int key = j0 + kr;
+      kreg[u] = key < kend ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * D + 8 * kc)
+                           : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < KG; ++r) {
+      const int key = j0 + KG * va + r;
+      vreg[r] = key < kend ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * D + 8 * vc)
+                           : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    __bf16* Ks = smem + buf * BUF;
+    __bf16* Vt = Ks + K_ELEMS;
+#pragma unroll
+    for (int u = 0; u < NK; ++u) {
+      const int ch = tid + kThreads * u;
+      const int kr = ch / (D / 8), kc = ch % (D / 8);
+      *reinterpret_cast<u32x4*>(Ks + kr * KSTR + 8 * kc) = kreg[u];
+    }
+    // transpose: column 8vc + i of the KG keys -> Vt row 8vc + i
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = i >> 1;
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      __bf16* dst = Vt + (8 * vc + i) * VSTR + KG * va;
+      if constexpr (KG == 4) {
+        u32x2 x;
+        x[0] = __builtin_amdgcn_perm(vreg[1][q], vreg[0][q], sel);
+        x[1] = __builtin_amdgcn_perm(vreg[3][q], vreg[2][q], sel);
+        *reinterpret_cast<u32x2*>(dst) = x;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(vreg[1][q], vreg[0][q], sel);
+      }
+    }
+  };
+
+  // per-lane state: output accumulator (O^T, row c, columns tau), running max / sum
+  f32x16 acc[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float cs = p.scale_log2;
+
+  // LDS read offsets (elements) that depend only on the lane
+  const int sig = (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1);          // key slot order
+  const int k_off = sig * KSTR + 8 * g;
+  // tau: output column of accumulator slot 8a + 4g' + b of tile i = (D/2)g' + 16i + 4a + b
+  const int tau0 = (D / 2) * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
+  const int v_off = tau0 * VSTR + 8 * g;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int j0 = it * BN;
+    if (it + 1 < ntiles) load_tile(j0 + BN);
+
+    if (it < ntw) {
+      const __bf16* Ks = smem + cur * BUF;
+      const __bf16* Vt = Ks + K_ELEMS;
+      // ---- S^T = K Q^T for 2 x 32 keys ----
+      f32x16 s[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        s[hh] = f32x16{};
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + 32 * hh * KSTR + k_off + 16 * t);
+          s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[hh], 0, 0, 0);
+        }
+      }
+      // ---- masks (edge tiles only): register r of s[hh] is key j0 + 32hh + 16(r/8) + 8g + r%8
+      const bool need_mask = (j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 32 * hh + 16 * (r >> 3) + 8 * g + (r & 7);
+            bool ok = key < kend;
+            if (CAUSAL) ok = ok && key <= row;
+            s[hh][r] = ok ? s[hh][r] : -__builtin_inff();
+          }
+      }
+      // ---- online softmax ----
+      float mx = s[0][0];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][r]);
+      mx = wave_max_pair(mx);
+      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * cs;
+      const float m_new = fmaxf(m_run, m_tile);
+      const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < NO; ++i) acc[i] *= alpha;
+      float lsum = l_run * alpha;
+
+      bf16x8 pk[2][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = s[hh][r];
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, cs, -base));
+          if (need_mask) pr = (x == -__builtin_inff()) ? 0.f : pr;
+          e[r] = pr;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          f32x8 e8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e8[j] = e[8 * m + j];
+          pk[hh][m] = __builtin_convertvector(e8, bf16x8);
+          // row sum of the rounded probabilities actually used below
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, lsum, false);
+          }
+        }
+      }
+      l_run = lsum;
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int i = 0; i < NO; ++i) {
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + v_off + 16 * i * VSTR + 32 * hh + 16 * m);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
+          }
+    }
+
+    if (it + 1 < ntiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane ----
+  if (row < Tq) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    __bf16* op = Og + (int64_t)row * D + (D / 2) * g;
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x8 o8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o8[j] = acc[i][8 * h2 + j] * inv;
+        *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel (v_mfma_f32_32x32x2_f32; probabilities stay fp32)
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool KEYPAD>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(Params p) {
+  constexpr int BN = 32;
+  constexpr int KSTR = D + 1;            // odd stride: the 32 key rows hit 32 banks
+  constexpr int VSTR = D + 8;            // the two lane halves read rows 4 apart: offset 32 banks
+  constexpr int K_ELEMS = BN * KSTR;
+  constexpr int V_ELEMS = BN * VSTR;
+  constexpr int BUF = K_ELEMS + V_ELEMS;
+  constexpr int DH = D / 2;              // S^T steps (2 d-values per step)
+  constexpr int NO = D / 32;
+  constexpr int NC = BN * D / 4 / kThreads;   // 16-byte chunks per thread per tensor
+
+  __shared__ __attribute__((aligned(16))) float smem[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, c = lane & 31;
+
+  int bh, qt;
+  tile_of_block(p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int q0 = qt * kBM;
+  const int qw = q0 + 32 * w;
+  const int row = qw + c;
+
+  int kend = Tk;
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  int kend_wg = kend;
+  if (CAUSAL) kend_wg = min(kend_wg, q0 + kBM);
+  const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
+  int kend_w = CAUSAL ? min(kend, qw + 32) : kend;
+  if (qw >= Tq) kend_w = 0;
+  const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
+
+  const float* Qg = static_cast<const float*>(p.q) + (int64_t)bh * Tq * D;
+  const float* Kg = static_cast<const float*>(p.k) + (int64_t)bh * Tk * D;
+  const float* Vg = static_cast<const float*>(p.v) + (int64_t)bh * Tk * D;
+  float* Og = static_cast<float*>(p.o) + (int64_t)bh * Tq * D;
+
+  // Q: d index of step t for lane half g is t + (D/2) g -> D/2 contiguous floats
+  float qf[DH];
+  {
+    const bool ok = row < Tq;
+    const float* qp = Qg + (int64_t)(ok ? row : 0) * D + DH * g;
+#pragma unroll
+    for (int t4 = 0; t4 < DH / 4; ++t4) {
+      f32x4 x = ok ? *reinterpret_cast<const f32x4*>(qp + 4 * t4) : f32x4{0, 0, 0, 0};
+      if (p.neg) x = -x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qf[4 * t4 + j] = x[j];
+    }
+  }
+
+  f32x4 kreg[NC], vreg[NC];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int ch = tid + kThreads * u;
+      const int kr = ch / (D / 4), kc = ch % (D / 4);
+      const int key = j0 + kr;
+      const bool ok = key < kend;
+      kreg[u] = ok ? *reinterpret_cast<const f32x4*>(Kg + (int64_t)key * D + 4 * kc) : f32x4{0, 0, 0, 0};
+      vreg[u] = ok ? *reinterpret_cast<const f32x4*>(Vg + (int64_t)key * D + 4 * kc) : f32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    float* Ks = smem + buf * BUF;
+    float* Vs = Ks + K_ELEMS;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int ch = tid + kThreads * u;
+      const int kr = ch / (D / 4), kc = ch % (D / 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Ks[kr * KSTR + 4 * kc + j] = kreg[u][j];
+      *reinterpret_cast<f32x4*>(Vs + kr * VSTR + 4 * kc) = vreg[u];
+    }
+  };
+
+  f32x16 acc[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+  const float cs = p.scale_log2;
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int j0 = it * BN;
+    if (it + 1 < ntiles) load_tile(j0 + BN);
+
+    if (it < ntw) {
+      const float* Ks = smem + cur * BUF;
+      const float* Vs = Ks + K_ELEMS;
+      // S^T: lane's accumulator register r is key 8(r/4) + 4g + r%4 of the tile
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DH; ++t)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[c * KSTR + t + DH * g], qf[t], s, 0, 0, 0);
+      const bool need_mask = (j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          bool ok = key < kend;
+          if (CAUSAL) ok = ok && key <= row;
+          s[r] = ok ? s[r] : -__builtin_inff();
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = wave_max_pair(mx);
+      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * cs;
+      const float m_new = fmaxf(m_run, m_tile);
+      const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < NO; ++i) acc[i] *= alpha;
+      float lsum = l_run * alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[r];
+        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, cs, -base));
+        if (need_mask) pr = (x == -__builtin_inff()) ? 0.f : pr;
+        s[r] = pr;
+        lsum += pr;
+      }
+      l_run = lsum;
+      // O^T += V^T P^T: step t contracts key 8(t/4) + 4g + t%4, i.e. this lane's register t
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int key = 8 * (t >> 2) + 4 * g + (t & 3);
+#pragma unroll
+        for (int i = 0; i < NO; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(Vs[key * VSTR + 32 * i + c], s[t], acc[i], 0, 0, 0);
+      }
+    }
+
+    if (it + 1 < ntiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds columns 32i + 8a + 4g + (0..3) of row c
+  if (row < Tq) {
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    float* op = Og + (int64_t)row * D;
+#pragma unroll
+    for (int i = 0; i < NO; ++i)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 o4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o4[j] = acc[i][4 * a + j] * inv;
+        *reinterpret_cast<f32x4*>(op + 32 * i + 8 * a + 4 * g) = o4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <int D, bool C, bool P>
+static const void* bf16_fn() { return reinterpret_cast<const void*>(&attn_fwd_bf16_kernel<D, C, P>); }
+template <int D, bool C, bool P>
+static const void* f32_fn() { return reinterpret_cast<const void*>(&attn_fwd_f32_kernel<D, C, P>); }
+
+template <int D>
+static const void* pick(bool f32, bool causal, bool keypad) {
+  if (f32) {
+    if (causal) return keypad ? f32_fn<D, true, true>() : f32_fn<D, true, false>();
+    return keypad ? f32_fn<D, false, true>() : f32_fn<D, false, false>();
+  }
+  if (causal) return keypad ? bf16_fn<D, true, true>() : bf16_fn<D, true, false>();
+  return keypad ? bf16_fn<D, false, true>() : bf16_fn<D, false, false>();
+}
+
+int rows_per_block() { return kBM; }
+
+hipError_t launch_fwd(const Params& prm, DType dt, int d, bool causal, bool keypad, hipStream_t stream) {
+  const void* fn = (d == 64) ? pick<64>(dt == DType::F32, causal, keypad)
+                             : pick<128>(dt == DType::F32, causal, keypad);
+  Params local = prm;
+  void* args[] = {&local};
+  return hipLaunchKernel(fn, dim3(prm.n_wg), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace attn
