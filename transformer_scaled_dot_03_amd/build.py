@@ -54,6 +54,9 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
             msg = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
             if msg.strip():
                 print(msg, file=sys.stderr)
+        # every kernel stub and entry point must resolve: load it now (RTLD_NOW)
+        import ctypes
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
         os.replace(tmp, LIB_PATH)
     finally:
         if os.path.exists(tmp):

@@ -63,7 +63,10 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
   p.H = h;
   p.Tq = Tq;
   p.Tk = Tk;
-  p.scale_log2 = static_cast<float>(std::fabs(static_cast<double>(scale)) * 1.4426950408889634);
+  // |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always map to
+  // exp2(-inf) = 0; for scale = 0 every exp2 argument then rounds to 0 and the
+  // weights are exactly uniform, as for a true zero.
+  p.scale_log2 = static_cast<float>(std::fmax(std::fabs(static_cast<double>(scale)) * 1.4426950408889634, 1e-30));
   p.neg = scale < 0.f ? 1 : 0;
   p.n_qtiles = static_cast<int>(n_qtiles);
   p.n_wg = static_cast<int>(n_wg);

@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_launch.h"
 
 namespace attn {
@@ -57,6 +59,26 @@ constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 
 
 __device__ __forceinline__ float wave_max_pair(float x) {
   return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+// Lanes l and l ^ 32 hold the two halves of one query row: after
+// v_permlane32_swap the two results hold x of lane l and of lane l ^ 32 (in
+// some order), so their max / sum is the pair's.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Raw buffer resource over [base, base + bytes): loads at or past `bytes`
+// return zero (hardware range check), which zero-fills keys past the valid
+// length without a branch.  Word 3 = 0x00020000: the gfx9 data-format field
+// for untyped dword loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // Work-group id -> (b*h + head, query tile).  The hardware hands consecutive
@@ -82,25 +104,65 @@ __device__ __forceinline__ int clamp_len(const int32_t* key_lens, int b, int Tk)
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+
+// Running-max update threshold (log2 units).  The accumulator is rescaled only
+// when some row's tile maximum exceeds the reference maximum by more than
+// this; otherwise the stale reference is kept and the probabilities are at
+// most 2^8 (exact softmax either way: the reference cancels in O / l).
+constexpr float kRescaleThreshold = 8.0f;
+
+// key slot order: slot s of a 32-key slice holds key sigma(s) (bits 2 and 3 swapped)
+__device__ __forceinline__ int sigma32(int s) { return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1); }
+
+// LDS tiles of K and V are D*2-byte rows of 16-byte chunks, written by
+// direct-to-LDS buffer loads (lane l of a load fills bytes 16 l of a 1 KB
+// block) and stored XOR-swizzled: physical chunk = logical chunk ^ swz(row).
+// K rows are in key-slot order (row 32 hh + s holds key 32 hh + sigma(s)), so
+// the A-operand read of S^T is row c for lane c; the swizzle spreads the 16
+// lanes that read one chunk column over 16 different chunks.  V rows are in
+// key order; the swizzle makes the transposed reads (4 rows x 4 chunks per 16
+// lanes) hit distinct chunks.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  r &= 31;
+  return D == 128 ? (r & 15) : ((r ^ (r >> 3)) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  return D == 128 ? 2 * (r & 3) : 2 * ((r >> 1) & 1);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from buffer offset `off` straight into LDS at dst + 16 * lane
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+}
+
 template <int D, bool CAUSAL, bool KEYPAD>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
   constexpr int BN = 64;                 // keys per tile
-  constexpr int KSTR = D + 8;            // K row stride in LDS (elements): +16 B pad
-  constexpr int VSTR = BN + 8;           // Vt row stride in LDS (elements): +16 B pad
-  constexpr int K_ELEMS = BN * KSTR;
-  constexpr int V_ELEMS = D * VSTR;
-  constexpr int BUF = K_ELEMS + V_ELEMS;
+  constexpr int ROWB = D * 2;            // bytes per K / V row
+  constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
+  constexpr int NLD = TILEB / 1024 / kWaves;   // 1 KB direct loads per wave per tensor
   constexpr int DT = D / 16;             // MFMA steps over d for S^T
   constexpr int NO = D / 32;             // 32-column tiles of the output
-  constexpr int NK = BN * D / 8 / kThreads;   // 16-byte K chunks per thread
-  constexpr int KG = BN * D / 8 / kThreads;   // keys per thread in the V transpose
-  constexpr int NA = BN / KG;                 // key groups per tile
-  static_assert(KG == 2 || KG == 4, "tile shape");
+  static_assert(NLD >= 1 && TILEB % (1024 * kWaves) == 0, "tile shape");
+  constexpr float kNegInf = -__builtin_inff();
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * BUF];
+  // two buffers per tensor, as four distinct arrays: the compiler can then see
+  // that direct-to-LDS loads into one buffer never alias reads of the other,
+  // and does not wait for the prefetch before reading the current tile
+  __shared__ __attribute__((aligned(1024))) char k_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c = lane & 31;
 
   int bh, qt;
@@ -138,168 +200,152 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // staging registers for one K/V tile
-  u32x4 kreg[NK];
-  u32x4 vreg[KG];
-  const int va = tid % NA, vc = tid / NA;   // V unit: keys KG*va .., columns 8vc ..
+  // ---- direct-to-LDS staging: this lane's source offsets for its NLD 1 KB blocks
+  uint32_t k_src[NLD], v_src[NLD];
+#pragma unroll
+  for (int u = 0; u < NLD; ++u) {
+    const int pos = (kWaves * u + w) * 1024 + 16 * lane;
+    const int r = pos / ROWB, pc = (pos % ROWB) / 16;
+    const int key = (r & 32) + sigma32(r & 31);
+    k_src[u] = key * ROWB + 16 * (pc ^ k_swz<D>(r));
+    v_src[u] = r * ROWB + 16 * (pc ^ v_swz<D>(r));
+  }
+  // rows at or past kend read as zero (buffer range check)
+  auto load_tile = [&](int j0, char* kt, char* vt) {
+    const uint32_t bytes = (uint32_t)(kend - j0) * ROWB;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int blk = (kWaves * u + w) * 1024;
+      lds_dma16(kr, kt + blk, k_src[u]);
+      lds_dma16(vr, vt + blk, v_src[u]);
+    }
+  };
 
-  auto load_tile = [&](int j0) {
+  // ---- LDS read offsets (bytes, within a tile)
+  // K: lane (c, g), step t reads logical chunk 2t + g of slot row 32 hh + c
+  int k_rd[DT];
 #pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int ch = tid + kThreads * u;
-      const int kr = ch / (D / 8), kc = ch % (D / 8);
-      const int key = j0 + kr;
-      kreg[u] = key < kend ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * D + 8 * kc)
-                           : u32x4{0, 0, 0, 0};
-    }
+  for (int t = 0; t < DT; ++t) k_rd[t] = c * ROWB + 16 * ((2 * t + g) ^ k_swz<D>(c));
+  // V^T via transposed reads: in each 16-lane group G (h = G & 1, g = G >> 1)
+  // source lane s reads 4 consecutive output columns of key row
+  // 8g + e0 + s/4 (+ 32 hh + 16 m); output lane j then holds that column of
+  // keys e0 .. e0+3 -- the A operand of O^T = V^T P^T.
+  int v_rd[NO];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    const int h = G & 1, gg = G >> 1;
+    const int r = 8 * gg + (sl >> 2);
 #pragma unroll
-    for (int r = 0; r < KG; ++r) {
-      const int key = j0 + KG * va + r;
-      vreg[r] = key < kend ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * D + 8 * vc)
-                           : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < NO; ++i) {
+      const int lc = (D / 16) * (sl & 1) + 2 * i + h;
+      v_rd[i] = r * ROWB + 16 * (lc ^ v_swz<D>(r)) + 8 * ((sl >> 1) & 1);
     }
-  };
-  auto store_tile = [&](int buf) {
-    __bf16* Ks = smem + buf * BUF;
-    __bf16* Vt = Ks + K_ELEMS;
-#pragma unroll
-    for (int u = 0; u < NK; ++u) {
-      const int ch = tid + kThreads * u;
-      const int kr = ch / (D / 8), kc = ch % (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + kr * KSTR + 8 * kc) = kreg[u];
-    }
-    // transpose: column 8vc + i of the KG keys -> Vt row 8vc + i
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = i >> 1;
-      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      __bf16* dst = Vt + (8 * vc + i) * VSTR + KG * va;
-      if constexpr (KG == 4) {
-        u32x2 x;
-        x[0] = __builtin_amdgcn_perm(vreg[1][q], vreg[0][q], sel);
-        x[1] = __builtin_amdgcn_perm(vreg[3][q], vreg[2][q], sel);
-        *reinterpret_cast<u32x2*>(dst) = x;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(vreg[1][q], vreg[0][q], sel);
-      }
-    }
-  };
+  }
 
   // per-lane state: output accumulator (O^T, row c, columns tau), running max / sum
   f32x16 acc[NO];
 #pragma unroll
   for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run = kNegInf;   // reference maximum (scaled, log2 units)
+  float base = 0.f;        // m_run, or 0 while no key has been seen
+  float l_run = 0.f;       // this lane's half of the row sum
   const float cs = p.scale_log2;
-
-  // LDS read offsets (elements) that depend only on the lane
-  const int sig = (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1);          // key slot order
-  const int k_off = sig * KSTR + 8 * g;
-  // tau: output column of accumulator slot 8a + 4g' + b of tile i = (D/2)g' + 16i + 4a + b
-  const int tau0 = (D / 2) * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3);
-  const int v_off = tau0 * VSTR + 8 * g;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const int j0 = it * BN;
-    if (it + 1 < ntiles) load_tile(j0 + BN);
-
-    if (it < ntw) {
-      const __bf16* Ks = smem + cur * BUF;
-      const __bf16* Vt = Ks + K_ELEMS;
-      // ---- S^T = K Q^T for 2 x 32 keys ----
-      f32x16 s[2];
+  // one 64-key tile: S^T, softmax update, O^T += V^T P^T.  `need_mask` (wave
+  // uniform) is set on edge tiles only; masked scores become -inf and, since
+  // cs > 0, exp2 gives them exactly zero weight.
+  auto tile = [&](int j0, bool need_mask, const char* kt, const char* vt) {
+    f32x16 s[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        s[hh] = f32x16{};
+    for (int hh = 0; hh < 2; ++hh) {
+      s[hh] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Ks + 32 * hh * KSTR + k_off + 16 * t);
-          s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[hh], 0, 0, 0);
-        }
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + k_rd[t]);
+        s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[hh], 0, 0, 0);
       }
-      // ---- masks (edge tiles only): register r of s[hh] is key j0 + 32hh + 16(r/8) + 8g + r%8
-      const bool need_mask = (j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j0 + 32 * hh + 16 * (r >> 3) + 8 * g + (r & 7);
-            bool ok = key < kend;
-            if (CAUSAL) ok = ok && key <= row;
-            s[hh][r] = ok ? s[hh][r] : -__builtin_inff();
-          }
-      }
-      // ---- online softmax ----
-      float mx = s[0][0];
+    }
+    // register r of s[hh] holds key j0 + 32hh + 16(r/8) + 8g + r%8
+    if (need_mask) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][r]);
-      mx = wave_max_pair(mx);
-      const float m_tile = (mx == -__builtin_inff()) ? mx : mx * cs;
-      const float m_new = fmaxf(m_run, m_tile);
-      const float base = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < NO; ++i) acc[i] *= alpha;
-      float lsum = l_run * alpha;
-
-      bf16x8 pk[2][2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x16 e;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float x = s[hh][r];
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(x, cs, -base));
-          if (need_mask) pr = (x == -__builtin_inff()) ? 0.f : pr;
-          e[r] = pr;
+          const int key = j0 + 32 * hh + 16 * (r >> 3) + 8 * g + (r & 7);
+          bool ok = key < kend;
+          if (CAUSAL) ok = ok && key <= row;
+          s[hh][r] = ok ? s[hh][r] : kNegInf;
         }
+    }
+    float mx = s[0][0];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8 e8;
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) e8[j] = e[8 * m + j];
-          pk[hh][m] = __builtin_convertvector(e8, bf16x8);
-          // row sum of the rounded probabilities actually used below
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][r]);
+    const float m_tile = pair_max(mx) * cs;            // -inf if the row has no key here
+    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - b_new);   // 0 when m_run = -inf
+      m_run = m_new;
+      base = b_new;
+      l_run *= alpha;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, lsum, false);
-          }
+      for (int i = 0; i < NO; ++i) acc[i] *= alpha;
+    }
+    bf16x8 pk[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x8 e8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hh][8 * m + j], cs, -base));
+        pk[hh][m] = __builtin_convertvector(e8, bf16x8);
+        // row sum of the rounded probabilities actually used below
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run, false);
         }
       }
-      l_run = lsum;
-      // ---- O^T += V^T P^T ----
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-          for (int i = 0; i < NO; ++i) {
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + v_off + 16 * i * VSTR + 32 * hh + 16 * m);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
-          }
-    }
+        for (int i = 0; i < NO; ++i) {
+          const char* vb = vt + (32 * hh + 16 * m) * ROWB + v_rd[i];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
+        }
+  };
 
-    if (it + 1 < ntiles) store_tile(cur ^ 1);
-    __syncthreads();
+  // one pipeline step: prefetch tile it+1 into (kn, vn), compute tile it from (kc, vc)
+  auto step = [&](int it, const char* kc, const char* vc, char* kn, char* vn) {
+    const int j0 = it * BN;
+    if (it + 1 < ntiles) load_tile(j0 + BN, kn, vn);
+    if (it < ntw) tile(j0, (j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw), kc, vc);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tile have landed
+    __syncthreads();                 // ... and every wave's; the current buffer is free
+  };
+
+  if (ntiles > 0) load_tile(0, k_lds0, v_lds0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it += 2) {
+    step(it, k_lds0, v_lds0, k_lds1, v_lds1);
+    if (it + 1 < ntiles) step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
   }
 
   // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane ----
+  const float l_tot = pair_sum(l_run);
   if (row < Tq) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     __bf16* op = Og + (int64_t)row * D + (D / 2) * g;
 #pragma unroll
