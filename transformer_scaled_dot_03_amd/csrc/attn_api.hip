@@ -41,7 +41,7 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
     return ATTN_ERR_ALIGN;
   if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
 
-  const int64_t bm = attn::rows_per_block();
+  const int64_t bm = attn::rows_per_block(dt, d_k);
   const int64_t bh = static_cast<int64_t>(B) * h;
   const int64_t n_qtiles = (Tq + bm - 1) / bm;
   const int64_t n_wg = bh * n_qtiles;  // B, h < 2^31 and n_qtiles < 2^25: no overflow

@@ -141,24 +141,83 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* dst, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
+// Shape of the bf16 kernel per head size: waves per work-group (each wave
+// owns 32 query rows) and K/V tile buffers per tensor (prefetch distance
+// kBuf - 1 tiles).  d = 128 uses one 8-wave work-group per CU with four
+// buffers (128 KB of LDS); d = 64 two or more 4-wave work-groups per CU.
+template <int D>
+struct Bf16Shape;
+template <>
+struct Bf16Shape<64> {
+  static constexpr int kWaves = 4, kBuf = 2;
+};
+template <>
+struct Bf16Shape<128> {
+  static constexpr int kWaves = 8, kBuf = 2;
+};
+
+// Work-group barrier for the K/V pipeline: first wait until at most N of
+// this wave's vector-memory operations (the direct-to-LDS prefetches issued
+// last) are outstanding and all its LDS reads have returned, then s_barrier.
+// A plain __syncthreads() would also wait for the newest prefetch (its
+// release fence covers the LDS writes those loads make).
+template <int N>
+__device__ __forceinline__ void pipeline_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));   // vmcnt N, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+}
+
+// calls f(integral_constant<int, U>) for U = U0 .. UN-1
+template <int U0, int UN, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (U0 < UN) {
+    f(std::integral_constant<int, U0>{});
+    static_for<U0 + 1, UN>(f);
+  }
+}
+
 template <int D, bool CAUSAL, bool KEYPAD>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
+__global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_kernel(Params p) {
+  constexpr int WAVES = Bf16Shape<D>::kWaves;
+  constexpr int NBUF = Bf16Shape<D>::kBuf;   // tile buffers per tensor
+  constexpr int UNR = NBUF % 2 == 0 ? NBUF : 2 * NBUF;   // steps per loop trip
   constexpr int BN = 64;                 // keys per tile
+  constexpr int BM = 32 * WAVES;         // query rows per work-group
   constexpr int ROWB = D * 2;            // bytes per K / V row
   constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
-  constexpr int NLD = TILEB / 1024 / kWaves;   // 1 KB direct loads per wave per tensor
+  constexpr int NLD = TILEB / 1024 / WAVES;   // 1 KB direct loads per wave per tile
   constexpr int DT = D / 16;             // MFMA steps over d for S^T
   constexpr int NO = D / 32;             // 32-column tiles of the output
-  static_assert(NLD >= 1 && TILEB % (1024 * kWaves) == 0, "tile shape");
+  static_assert(NLD >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
+  static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
   constexpr float kNegInf = -__builtin_inff();
 
-  // two buffers per tensor, as four distinct arrays: the compiler can then see
-  // that direct-to-LDS loads into one buffer never alias reads of the other,
+  // NBUF buffers per tensor, each its own array: the compiler can then see
+  // that direct-to-LDS loads into one buffer never alias reads of another,
   // and does not wait for the prefetch before reading the current tile
-  __shared__ __attribute__((aligned(1024))) char k_lds0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb2[NBUF > 2 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char kb3[NBUF > 3 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb2[NBUF > 2 ? TILEB : 16];
+  __shared__ __attribute__((aligned(1024))) char vb3[NBUF > 3 ? TILEB : 16];
+  auto kbuf = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value % NBUF;
+    if constexpr (i == 0) return kb0;
+    else if constexpr (i == 1) return kb1;
+    else if constexpr (i == 2) return kb2;
+    else return kb3;
+  };
+  auto vbuf = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value % NBUF;
+    if constexpr (i == 0) return vb0;
+    else if constexpr (i == 1) return vb1;
+    else if constexpr (i == 2) return vb2;
+    else return vb3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -169,14 +228,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
   tile_of_block(p.n_qtiles, CAUSAL, bh, qt);
   const int b = bh / p.H;
   const int Tq = p.Tq, Tk = p.Tk;
-  const int q0 = qt * kBM;
+  const int q0 = qt * BM;
   const int qw = q0 + 32 * w;          // first row of this wave
   const int row = qw + c;              // this lane's query row
 
   int kend = Tk;                       // keys [0, kend) hold data
   if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
   int kend_wg = kend;
-  if (CAUSAL) kend_wg = min(kend_wg, q0 + kBM);
+  if (CAUSAL) kend_wg = min(kend_wg, q0 + BM);
   const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
   int kend_w = CAUSAL ? min(kend, qw + 32) : kend;
   if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
@@ -204,23 +263,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
   uint32_t k_src[NLD], v_src[NLD];
 #pragma unroll
   for (int u = 0; u < NLD; ++u) {
-    const int pos = (kWaves * u + w) * 1024 + 16 * lane;
+    const int pos = (WAVES * u + w) * 1024 + 16 * lane;
     const int r = pos / ROWB, pc = (pos % ROWB) / 16;
     const int key = (r & 32) + sigma32(r & 31);
     k_src[u] = key * ROWB + 16 * (pc ^ k_swz<D>(r));
     v_src[u] = r * ROWB + 16 * (pc ^ v_swz<D>(r));
   }
   // rows at or past kend read as zero (buffer range check)
-  auto load_tile = [&](int j0, char* kt, char* vt) {
-    const uint32_t bytes = (uint32_t)(kend - j0) * ROWB;
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, bytes);
+  auto load_k = [&](int j0, char* kt) {
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, (uint32_t)(kend - j0) * ROWB);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int blk = (kWaves * u + w) * 1024;
-      lds_dma16(kr, kt + blk, k_src[u]);
-      lds_dma16(vr, vt + blk, v_src[u]);
-    }
+    for (int u = 0; u < NLD; ++u) lds_dma16(kr, kt + (WAVES * u + w) * 1024, k_src[u]);
+  };
+  auto load_v = [&](int j0, char* vt) {
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, (uint32_t)(kend - j0) * ROWB);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) lds_dma16(vr, vt + (WAVES * u + w) * 1024, v_src[u]);
   };
 
   // ---- LDS read offsets (bytes, within a tile)
@@ -244,21 +302,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     }
   }
 
-  // per-lane state: output accumulator (O^T, row c, columns tau), running max / sum
+  // per-lane state: output accumulator (O^T, row c, columns tau), reference
+  // maximum (scaled, log2 units), its offset (0 while no key has been seen),
+  // this lane's half of the row sum
   f32x16 acc[NO];
 #pragma unroll
   for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
-  float m_run = kNegInf;   // reference maximum (scaled, log2 units)
-  float base = 0.f;        // m_run, or 0 while no key has been seen
-  float l_run = 0.f;       // this lane's half of the row sum
+  float m_run = kNegInf, base = 0.f, l_run = 0.f;
   const float cs = p.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // one 64-key tile: S^T, softmax update, O^T += V^T P^T.  `need_mask` (wave
-  // uniform) is set on edge tiles only; masked scores become -inf and, since
-  // cs > 0, exp2 gives them exactly zero weight.
-  auto tile = [&](int j0, bool need_mask, const char* kt, const char* vt) {
-    f32x16 s[2];
+  // S^T = K Q^T for the 64 keys of a K tile: register e of s[hh] holds key
+  // 32hh + 16(e/8) + 8g + e%8 of the tile
+  auto scores = [&](const char* kt, f32x16 (&s)[2]) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       s[hh] = f32x16{};
@@ -268,79 +324,112 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[hh], 0, 0, 0);
       }
     }
-    // register r of s[hh] holds key j0 + 32hh + 16(r/8) + 8g + r%8
-    if (need_mask) {
+  };
+
+  // Software pipeline, one 64-key tile per step: the matrix cores compute the
+  // scores of tile j+1 while the vector ALUs turn the scores of tile j into
+  // probabilities, then O^T += V^T P^T for tile j.  K is therefore staged one
+  // tile ahead of V: step j reads K(j+1) and V(j) and prefetches
+  // K(j+NBUF) and V(j+NBUF-1), then waits only for the tiles the next step reads.
+  // Masked scores (edge tiles only; the test is wave uniform) become -inf and,
+  // since cs > 0, exp2 gives them exactly zero weight.
+  f32x16 s2[2][2];
+  auto step = [&](int it, auto U) {
+    constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
+    f32x16 (&sc)[2] = s2[u & 1];
+    f32x16 (&sn)[2] = s2[(u + 1) & 1];
+    const int j0 = it * BN;
+    if (it + NBUF < ntiles) load_k(j0 + NBUF * BN, kbuf(std::integral_constant<int, u>{}));
+    if (it + NBUF - 1 < ntiles) load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
+    if (it < ntw) {
+      if ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw)) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+            bool ok = key < kend;
+            if (CAUSAL) ok = ok && key <= row;
+            sc[hh][e] = ok ? sc[hh][e] : kNegInf;
+          }
+      }
+      float mx = sc[0][0];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * hh + 16 * (r >> 3) + 8 * g + (r & 7);
-          bool ok = key < kend;
-          if (CAUSAL) ok = ok && key <= row;
-          s[hh][r] = ok ? s[hh][r] : kNegInf;
-        }
-    }
-    float mx = s[0][0];
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[hh][e]);
+      const float m_tile = pair_max(mx) * cs;             // -inf if the row has no key here
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - b_new);   // 0 when m_run = -inf
+        m_run = m_new;
+        base = b_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][r]);
-    const float m_tile = pair_max(mx) * cs;            // -inf if the row has no key here
-    if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float b_new = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - b_new);   // 0 when m_run = -inf
-      m_run = m_new;
-      base = b_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < NO; ++i) acc[i] *= alpha;
-    }
-    bf16x8 pk[2][2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        f32x8 e8;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[hh][8 * m + j], cs, -base));
-        pk[hh][m] = __builtin_convertvector(e8, bf16x8);
-        // row sum of the rounded probabilities actually used below
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run, false);
-        }
+        for (int i = 0; i < NO; ++i) acc[i] *= alpha;
       }
+      // scores of the next tile (unused past the wave's last tile)
+      scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+      bf16x8 pk[2][2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m) {
+          f32x8 e8;
 #pragma unroll
-        for (int i = 0; i < NO; ++i) {
-          const char* vb = vt + (32 * hh + 16 * m) * ROWB + v_rd[i];
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
+          for (int j = 0; j < 8; ++j)
+            e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hh][8 * m + j], cs, -base));
+          pk[hh][m] = __builtin_convertvector(e8, bf16x8);
+          // row sum of the rounded probabilities actually used below
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run, false);
+          }
         }
+      const char* v_cur = vbuf(std::integral_constant<int, u>{});
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int i = 0; i < NO; ++i) {
+            const char* vb = v_cur + (32 * hh + 16 * m) * ROWB + v_rd[i];
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
+            const bf16x8 vf =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
+          }
+    }
+    // The next step reads K(it+2) and V(it+1), loaded by step it+2-NBUF:
+    // only the loads of the NBUF-2 most recent steps may stay in flight.
+    int batches = 0;
+#pragma unroll
+    for (int k = 0; k < NBUF - 2; ++k) {
+      const int sk = it - k;
+      if (sk >= 0) batches += (sk + NBUF < ntiles) + (sk + NBUF - 1 < ntiles);
+    }
+    static_for<0, 2 * (NBUF - 2) + 1>([&](auto N) {
+      if (batches == N) pipeline_barrier<N * NLD>();
+    });
   };
 
-  // one pipeline step: prefetch tile it+1 into (kn, vn), compute tile it from (kc, vc)
-  auto step = [&](int it, const char* kc, const char* vc, char* kn, char* vn) {
-    const int j0 = it * BN;
-    if (it + 1 < ntiles) load_tile(j0 + BN, kn, vn);
-    if (it < ntw) tile(j0, (j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw), kc, vc);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tile have landed
-    __syncthreads();                 // ... and every wave's; the current buffer is free
-  };
-
-  if (ntiles > 0) load_tile(0, k_lds0, v_lds0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; it += 2) {
-    step(it, k_lds0, v_lds0, k_lds1, v_lds1);
-    if (it + 1 < ntiles) step(it + 1, k_lds1, v_lds1, k_lds0, v_lds0);
+  // prologue: K(0 .. NBUF-1) and V(0 .. NBUF-2), then the scores of tile 0
+  static_for<0, NBUF>([&](auto I) {
+    if (I < ntiles) load_k(I * BN, kbuf(I));
+  });
+  static_for<0, NBUF - 1>([&](auto I) {
+    if (I < ntiles) load_v(I * BN, vbuf(I));
+  });
+  pipeline_barrier<0>();
+  if (ntw > 0) scores(kb0, s2[0]);
+  pipeline_barrier<0>();             // K(0) consumed: its buffer takes K(NBUF)
+  for (int it0 = 0; it0 < ntiles; it0 += UNR) {
+    static_for<0, UNR>([&](auto U) {
+      if (it0 + U < ntiles) step(it0 + U, U);
+    });
   }
 
   // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane ----
@@ -549,14 +638,19 @@ static const void* pick(bool f32, bool causal, bool keypad) {
   return keypad ? bf16_fn<D, false, true>() : bf16_fn<D, false, false>();
 }
 
-int rows_per_block() { return kBM; }
+static int threads_per_block(DType dt, int d) {
+  if (dt == DType::F32) return kThreads;
+  return 64 * (d == 128 ? Bf16Shape<128>::kWaves : Bf16Shape<64>::kWaves);
+}
+
+int rows_per_block(DType dt, int d) { return threads_per_block(dt, d) / 2; }   // 32 rows per wave
 
 hipError_t launch_fwd(const Params& prm, DType dt, int d, bool causal, bool keypad, hipStream_t stream) {
   const void* fn = (d == 64) ? pick<64>(dt == DType::F32, causal, keypad)
                              : pick<128>(dt == DType::F32, causal, keypad);
   Params local = prm;
   void* args[] = {&local};
-  return hipLaunchKernel(fn, dim3(prm.n_wg), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(prm.n_wg), dim3(threads_per_block(dt, d)), args, 0, stream);
 }
 
 }  // namespace attn

@@ -21,11 +21,12 @@ struct Params {
   int B, H, Tq, Tk;
   float scale_log2;         // |scale| * log2(e): scores feed exp2
   int neg;                  // 1 when scale < 0: the kernel negates Q (exact)
-  int n_qtiles;             // ceil(Tq / rows_per_block())
+  int n_qtiles;             // ceil(Tq / rows_per_block(dt, d))
   int n_wg;                 // B * H * n_qtiles work-groups
 };
 
-int rows_per_block();
+// query rows per work-group of the kernel that serves (dt, d)
+int rows_per_block(DType dt, int d);
 hipError_t launch_fwd(const Params& p, DType dt, int d, bool causal, bool keypad, hipStream_t stream);
 
 }  // namespace attn
