@@ -141,19 +141,25 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* dst, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
 }
 
-// Shape of the bf16 kernel per head size: waves per work-group (each wave
-// owns 32 query rows) and K/V tile buffers per tensor (prefetch distance
-// kBuf - 1 tiles).  d = 128 uses one 8-wave work-group per CU with four
-// buffers (128 KB of LDS); d = 64 two or more 4-wave work-groups per CU.
+// Shape of the bf16 kernel per head size:
+//   kWaves  waves per work-group;
+//   kRG     groups of 32 query rows per wave: with 2, every K and V^T fragment
+//           read from LDS feeds two MFMAs (half the LDS reads per flop), at
+//           the price of ~400 registers (accumulators in AGPRs): one wave per SIMD;
+//   kBN     keys per pipeline step (the K/V tile);
+//   kBuf    K/V tile buffers per tensor (prefetch distance kBuf - 1 tiles).
+// Measured on MI355X for d = 128 (T = 16384): 8 waves x 1 group x 64 keys x 2
+// buffers is fastest; two row groups (one wave per SIMD) ran ~30% slower and
+// deeper prefetch (3 or 4 buffers) did not help.
 template <int D>
 struct Bf16Shape;
 template <>
 struct Bf16Shape<64> {
-  static constexpr int kWaves = 4, kBuf = 2;
+  static constexpr int kWaves = 4, kRG = 1, kBN = 64, kBuf = 2;
 };
 template <>
 struct Bf16Shape<128> {
-  static constexpr int kWaves = 8, kBuf = 2;
+  static constexpr int kWaves = 8, kRG = 1, kBN = 64, kBuf = 2;
 };
 
 // Work-group barrier for the K/V pipeline: first wait until at most N of
@@ -178,17 +184,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int D, bool CAUSAL, bool KEYPAD>
-__global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_kernel(Params p) {
+__global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) void attn_fwd_bf16_kernel(
+    Params p) {
   constexpr int WAVES = Bf16Shape<D>::kWaves;
+  constexpr int RG = Bf16Shape<D>::kRG;      // 32-row groups per wave
+  constexpr int BN = Bf16Shape<D>::kBN;      // keys per tile
   constexpr int NBUF = Bf16Shape<D>::kBuf;   // tile buffers per tensor
   constexpr int UNR = NBUF % 2 == 0 ? NBUF : 2 * NBUF;   // steps per loop trip
-  constexpr int BN = 64;                 // keys per tile
-  constexpr int BM = 32 * WAVES;         // query rows per work-group
-  constexpr int ROWB = D * 2;            // bytes per K / V row
-  constexpr int TILEB = BN * ROWB;       // bytes per K (or V) tile
-  constexpr int NLD = TILEB / 1024 / WAVES;   // 1 KB direct loads per wave per tile
-  constexpr int DT = D / 16;             // MFMA steps over d for S^T
-  constexpr int NO = D / 32;             // 32-column tiles of the output
+  constexpr int NH = BN / 32;                // 32-key slices per tile
+  constexpr int BM = 32 * RG * WAVES;        // query rows per work-group
+  constexpr int ROWB = D * 2;                // bytes per K / V row
+  constexpr int TILEB = BN * ROWB;           // bytes per K (or V) tile
+  constexpr int NLD = TILEB / 1024 / WAVES;  // 1 KB direct loads per wave per tile
+  constexpr int DT = D / 16;                 // MFMA steps over d for S^T
+  constexpr int NO = D / 32;                 // 32-column tiles of the output
+  static_assert(RG == 1 || RG == 2, "row groups");
+  static_assert(BN == 32 || BN == 64, "tile keys");
   static_assert(NLD >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
   static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
   constexpr float kNegInf = -__builtin_inff();
@@ -229,15 +240,14 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_ke
   const int b = bh / p.H;
   const int Tq = p.Tq, Tk = p.Tk;
   const int q0 = qt * BM;
-  const int qw = q0 + 32 * w;          // first row of this wave
-  const int row = qw + c;              // this lane's query row
+  const int qw = q0 + 32 * RG * w;     // first row of this wave; group r holds rows qw + 32r + c
 
   int kend = Tk;                       // keys [0, kend) hold data
   if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
   int kend_wg = kend;
   if (CAUSAL) kend_wg = min(kend_wg, q0 + BM);
   const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
-  int kend_w = CAUSAL ? min(kend, qw + 32) : kend;
+  int kend_w = CAUSAL ? min(kend, qw + 32 * RG) : kend;
   if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
   const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
 
@@ -247,15 +257,17 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_ke
   __bf16* Og = static_cast<__bf16*>(p.o) + (int64_t)bh * Tq * D;
 
   // Q rows -> registers (B operand of S^T); d index of step t is 16t + 8g + e.
-  bf16x8 qf[DT];
-  {
+  bf16x8 qf[RG][DT];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const int row = qw + 32 * r + c;
     const bool ok = row < Tq;
     const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * D + 8 * g;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
       if (p.neg) x ^= 0x80008000u;     // negative scale: use -Q and |scale| (exact)
-      qf[t] = __builtin_bit_cast(bf16x8, x);
+      qf[r][t] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
@@ -302,95 +314,117 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_ke
     }
   }
 
-  // per-lane state: output accumulator (O^T, row c, columns tau), reference
-  // maximum (scaled, log2 units), its offset (0 while no key has been seen),
-  // this lane's half of the row sum
-  f32x16 acc[NO];
+  // per-lane state of each row group: output accumulator (O^T, row c,
+  // columns tau), reference maximum (scaled, log2 units), its offset (0 while
+  // no key has been seen), this lane's half of the row sum
+  f32x16 acc[RG][NO];
+  float m_run[RG], base[RG], l_run[RG];
 #pragma unroll
-  for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
-  float m_run = kNegInf, base = 0.f, l_run = 0.f;
+  for (int r = 0; r < RG; ++r) {
+#pragma unroll
+    for (int i = 0; i < NO; ++i) acc[r][i] = f32x16{};
+    m_run[r] = kNegInf;
+    base[r] = 0.f;
+    l_run[r] = 0.f;
+  }
   const float cs = p.scale_log2;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T = K Q^T for the 64 keys of a K tile: register e of s[hh] holds key
-  // 32hh + 16(e/8) + 8g + e%8 of the tile
-  auto scores = [&](const char* kt, f32x16 (&s)[2]) {
+  // S^T = K Q^T for the BN keys of a K tile: register e of s[r][hh] holds
+  // key 32hh + 16(e/8) + 8g + e%8 of the tile for row qw + 32r + c
+  auto scores = [&](const char* kt, f32x16 (&s)[RG][NH]) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      s[hh] = f32x16{};
+    for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) s[r][hh] = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + k_rd[t]);
-        s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s[hh], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+          s[r][hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][t], s[r][hh], 0, 0, 0);
       }
     }
   };
 
-  // Software pipeline, one 64-key tile per step: the matrix cores compute the
+  // Software pipeline, one BN-key tile per step: the matrix cores compute the
   // scores of tile j+1 while the vector ALUs turn the scores of tile j into
   // probabilities, then O^T += V^T P^T for tile j.  K is therefore staged one
   // tile ahead of V: step j reads K(j+1) and V(j) and prefetches
-  // K(j+NBUF) and V(j+NBUF-1), then waits only for the tiles the next step reads.
+  // K(j+NBUF) and V(j+NBUF-1).
   // Masked scores (edge tiles only; the test is wave uniform) become -inf and,
   // since cs > 0, exp2 gives them exactly zero weight.
-  f32x16 s2[2][2];
+  f32x16 s2[2][RG][NH];
   auto step = [&](int it, auto U) {
     constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
-    f32x16 (&sc)[2] = s2[u & 1];
-    f32x16 (&sn)[2] = s2[(u + 1) & 1];
+    f32x16 (&sc)[RG][NH] = s2[u & 1];
+    f32x16 (&sn)[RG][NH] = s2[(u + 1) & 1];
     const int j0 = it * BN;
     if (it + NBUF < ntiles) load_k(j0 + NBUF * BN, kbuf(std::integral_constant<int, u>{}));
     if (it + NBUF - 1 < ntiles) load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
     if (it < ntw) {
       if ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw)) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int r = 0; r < RG; ++r)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-            bool ok = key < kend;
-            if (CAUSAL) ok = ok && key <= row;
-            sc[hh][e] = ok ? sc[hh][e] : kNegInf;
-          }
+          for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+              bool ok = key < kend;
+              if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
+              sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
+            }
       }
-      float mx = sc[0][0];
+      float m_tile[RG];
+      bool grow = false;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int r = 0; r < RG; ++r) {
+        float mx = sc[r][0][0];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[hh][e]);
-      const float m_tile = pair_max(mx) * cs;             // -inf if the row has no key here
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - b_new);   // 0 when m_run = -inf
-        m_run = m_new;
-        base = b_new;
-        l_run *= alpha;
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int i = 0; i < NO; ++i) acc[i] *= alpha;
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[r][hh][e]);
+        m_tile[r] = pair_max(mx) * cs;                 // -inf if the row has no key here
+        grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          const float m_new = fmaxf(m_run[r], m_tile[r]);
+          const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+          const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);   // 0 when m_run = -inf
+          m_run[r] = m_new;
+          base[r] = b_new;
+          l_run[r] *= alpha;
+#pragma unroll
+          for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
+        }
       }
       // scores of the next tile (unused past the wave's last tile)
       scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
-      bf16x8 pk[2][2];
+      bf16x8 pk[RG][NH][2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int r = 0; r < RG; ++r)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8 e8;
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[hh][8 * m + j], cs, -base));
-          pk[hh][m] = __builtin_convertvector(e8, bf16x8);
-          // row sum of the rounded probabilities actually used below
+          for (int m = 0; m < 2; ++m) {
+            f32x8 e8;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pr2 = {pk[hh][m][2 * j], pk[hh][m][2 * j + 1]};
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run, false);
+            for (int j = 0; j < 8; ++j)
+              e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
+            pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
+            // row sum of the rounded probabilities actually used below
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
+              l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
+            }
           }
-        }
       const char* v_cur = vbuf(std::integral_constant<int, u>{});
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -400,7 +434,9 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_ke
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
             const bf16x8 vf =
                 __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[hh][m], acc[i], 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+              acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[r][hh][m], acc[r][i], 0, 0, 0);
           }
     }
     // The next step reads K(it+2) and V(it+1), loaded by step it+2-NBUF:
@@ -433,18 +469,22 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 2) void attn_fwd_bf16_ke
   }
 
   // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane ----
-  const float l_tot = pair_sum(l_run);
-  if (row < Tq) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    __bf16* op = Og + (int64_t)row * D + (D / 2) * g;
 #pragma unroll
-    for (int i = 0; i < NO; ++i) {
+  for (int r = 0; r < RG; ++r) {
+    const int row = qw + 32 * r + c;
+    const float l_tot = pair_sum(l_run[r]);
+    if (row < Tq) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      __bf16* op = Og + (int64_t)row * D + (D / 2) * g;
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        f32x8 o8;
+      for (int i = 0; i < NO; ++i) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] = acc[i][8 * h2 + j] * inv;
-        *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 o8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) o8[j] = acc[r][i][8 * h2 + j] * inv;
+          *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
+        }
       }
     }
   }
@@ -643,7 +683,11 @@ static int threads_per_block(DType dt, int d) {
   return 64 * (d == 128 ? Bf16Shape<128>::kWaves : Bf16Shape<64>::kWaves);
 }
 
-int rows_per_block(DType dt, int d) { return threads_per_block(dt, d) / 2; }   // 32 rows per wave
+int rows_per_block(DType dt, int d) {
+  if (dt == DType::F32) return kBM;
+  return d == 128 ? 32 * Bf16Shape<128>::kRG * Bf16Shape<128>::kWaves
+                  : 32 * Bf16Shape<64>::kRG * Bf16Shape<64>::kWaves;
+}
 
 hipError_t launch_fwd(const Params& prm, DType dt, int d, bool causal, bool keypad, hipStream_t stream) {
   const void* fn = (d == 64) ? pick<64>(dt == DType::F32, causal, keypad)
