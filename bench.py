@@ -38,13 +38,52 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+KERNEL_SOURCES = ["attn_fwd_kernel.hip", "attn_launch.h", "attn_api.hip"]
+
+
 def kernel_source_digest() -> str:
+    """Short hash of the attention kernel sources (keys the committed counter data)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def mfma_ceiling(torch, dev, blocks=512, iters=5000, reps=3):
+    """What the bf16 matrix cores sustain here with random operands and no
+    memory traffic (libmfma_probe.so), and the shader clock meanwhile."""
+    import ctypes
+    path = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "libmfma_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    lib.mfma_probe_launch.restype = ctypes.c_int
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.mfma_probe_launch(sink.data_ptr(), clocks.data_ptr(), blocks, iters, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rc != 0:
+            return None
+        ms = e0.elapsed_time(e1)
+        c = clocks.view(-1, 2).double()
+        ghz = float((c[:, 0] / (c[:, 1] / 100e6)).mean()) / 1e9
+        tflops = blocks * 4 * iters * 16 * 32768.0 / (ms * 1e-3) / 1e12
+        if best is None or tflops > best["tflops"]:
+            best = {"tflops": round(tflops, 1), "clock_ghz": round(ghz, 3)}
+    best["what"] = ("v_mfma_f32_32x32x16_bf16 loop, random bf16 operands, no memory traffic, "
+                    f"{blocks} work-groups x 4 waves, best of {reps}")
+    return best
 
 
 def committed_traffic(workload: str, digest: str):
@@ -116,6 +155,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the pure-MFMA ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -209,6 +250,8 @@ def main():
         "hbm": {"compulsory_bytes": cb, "achieved_GBs": round(cb / (ev_ms * 1e-3) / 1e9, 1),
                 "peak_GBs": PEAK_HBM_GBS},
     }
+    if not args.no_mfma_probe and w.dtype == "bf16":
+        rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, kl, args.cpu_budget)
     print(json.dumps(rec), flush=True)

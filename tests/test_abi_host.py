@@ -135,3 +135,22 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(_lib.LibraryMissing):
         _lib.attn_version()
+
+
+def test_mfma_probe_library_exports_and_rejects_bad_arguments():
+    """The benchmark's pure-MFMA probe library loads and validates before launching."""
+    from transformer_scaled_dot_03_amd import build
+    if not os.path.exists(build.PROBE_LIB_PATH):
+        build.build()
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    header = open(os.path.join(ROOT, "include", "mfma_probe.h")).read()
+    header = re.sub(r"/\*.*?\*/", "", header, flags=re.S)
+    for name in set(re.findall(r"\b(mfma_probe_\w+)\s*\(", header)):
+        assert hasattr(lib, name), name
+    fn = lib.mfma_probe_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(None, 0x1000, 4, 4, None) == -1
+    assert fn(0x1000, None, 4, 4, None) == -1
+    assert fn(0x1000, 0x2000, 0, 4, None) == -1
+    assert fn(0x1000, 0x2000, 4, 0, None) == -1

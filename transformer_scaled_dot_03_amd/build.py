@@ -21,6 +21,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["attn_fwd_kernel.hip", "attn_api.hip"]
+# measurement aid for the benchmark: pure matrix-core loop (include/mfma_probe.h)
+PROBE_LIB_PATH = os.path.join(PKG, "libmfma_probe.so")
+PROBE_SOURCES = ["mfma_probe.hip"]
+TARGETS = [(LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code (kept out on
@@ -40,9 +44,15 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every source into LIB_PATH (always recompiles); return the path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".libattn.", suffix=".so.tmp", dir=PKG)
+    """Compile every library (always recompiles); return the attention library's path."""
+    for path, sources in TARGETS:
+        _build_one(path, sources, verbose, extra_flags)
+    return LIB_PATH
+
+
+def _build_one(lib_path: str, sources: list[str], verbose: bool, extra_flags: list[str] | None) -> None:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    fd, tmp = tempfile.mkstemp(prefix=".lib.", suffix=".so.tmp", dir=PKG)
     os.close(fd)
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
     try:
@@ -57,11 +67,10 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         # every kernel stub and entry point must resolve: load it now (RTLD_NOW)
         import ctypes
         ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
-        os.replace(tmp, LIB_PATH)
+        os.replace(tmp, lib_path)
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
-    return LIB_PATH
 
 
 if __name__ == "__main__":
