@@ -147,7 +147,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, char* dst, u
 //           read from LDS feeds two MFMAs (half the LDS reads per flop), at
 //           the price of ~400 registers (accumulators in AGPRs): one wave per SIMD;
 //   kBN     keys per pipeline step (the K/V tile);
-//   kBuf    K/V tile buffers per tensor (prefetch distance kBuf - 1 tiles).
+//   kBuf    K/V tile buffers per tensor (prefetch distance kBuf - 1 tiles);
+//   kPipe   compute the next tile's scores while the current tile's softmax
+//           runs (K staged one tile ahead of V); else scores, softmax and PV
+//           of a tile in sequence, K and V staged together.
 // Measured on MI355X for d = 128 (T = 16384): 8 waves x 1 group x 64 keys x 2
 // buffers is fastest; two row groups (one wave per SIMD) ran ~30% slower and
 // deeper prefetch (3 or 4 buffers) did not help.
@@ -156,10 +159,12 @@ struct Bf16Shape;
 template <>
 struct Bf16Shape<64> {
   static constexpr int kWaves = 4, kRG = 1, kBN = 64, kBuf = 2;
+  static constexpr bool kPipe = true;
 };
 template <>
 struct Bf16Shape<128> {
   static constexpr int kWaves = 8, kRG = 1, kBN = 64, kBuf = 2;
+  static constexpr bool kPipe = true;
 };
 
 // Work-group barrier for the K/V pipeline: first wait until at most N of
@@ -190,6 +195,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   constexpr int RG = Bf16Shape<D>::kRG;      // 32-row groups per wave
   constexpr int BN = Bf16Shape<D>::kBN;      // keys per tile
   constexpr int NBUF = Bf16Shape<D>::kBuf;   // tile buffers per tensor
+  constexpr bool PIPE = Bf16Shape<D>::kPipe;
   constexpr int UNR = NBUF % 2 == 0 ? NBUF : 2 * NBUF;   // steps per loop trip
   constexpr int NH = BN / 32;                // 32-key slices per tile
   constexpr int BM = 32 * RG * WAVES;        // query rows per work-group
@@ -199,7 +205,8 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   constexpr int DT = D / 16;                 // MFMA steps over d for S^T
   constexpr int NO = D / 32;                 // 32-column tiles of the output
   static_assert(RG == 1 || RG == 2, "row groups");
-  static_assert(BN == 32 || BN == 64, "tile keys");
+  static_assert(BN == 32 || BN == 64 || BN == 128, "tile keys");
+  static_assert(PIPE || NBUF == 2, "the sequential step uses plain double buffering");
   static_assert(NLD >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
   static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
   constexpr float kNegInf = -__builtin_inff();
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   for (int u = 0; u < NLD; ++u) {
     const int pos = (WAVES * u + w) * 1024 + 16 * lane;
     const int r = pos / ROWB, pc = (pos % ROWB) / 16;
-    const int key = (r & 32) + sigma32(r & 31);
+    const int key = (r & ~31) + sigma32(r & 31);
     k_src[u] = key * ROWB + 16 * (pc ^ k_swz<D>(r));
     v_src[u] = r * ROWB + 16 * (pc ^ v_swz<D>(r));
   }
@@ -354,118 +361,170 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   // K(j+NBUF) and V(j+NBUF-1).
   // Masked scores (edge tiles only; the test is wave uniform) become -inf and,
   // since cs > 0, exp2 gives them exactly zero weight.
-  f32x16 s2[2][RG][NH];
-  auto step = [&](int it, auto U) {
-    constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
-    f32x16 (&sc)[RG][NH] = s2[u & 1];
-    f32x16 (&sn)[RG][NH] = s2[(u + 1) & 1];
-    const int j0 = it * BN;
-    if (it + NBUF < ntiles) load_k(j0 + NBUF * BN, kbuf(std::integral_constant<int, u>{}));
-    if (it + NBUF - 1 < ntiles) load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
-    if (it < ntw) {
-      if ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw)) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r)
-#pragma unroll
-          for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-              bool ok = key < kend;
-              if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
-              sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
-            }
-      }
-      float m_tile[RG];
-      bool grow = false;
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        float mx = sc[r][0][0];
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[r][hh][e]);
-        m_tile[r] = pair_max(mx) * cs;                 // -inf if the row has no key here
-        grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          const float m_new = fmaxf(m_run[r], m_tile[r]);
-          const float b_new = (m_new == kNegInf) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);   // 0 when m_run = -inf
-          m_run[r] = m_new;
-          base[r] = b_new;
-          l_run[r] *= alpha;
-#pragma unroll
-          for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
-        }
-      }
-      // scores of the next tile (unused past the wave's last tile)
-      scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
-      bf16x8 pk[RG][NH][2];
+  // mask (edge tiles only; the test is wave uniform), running max with lazy
+  // rescale; masked scores become -inf and, since cs > 0, exp2 gives them
+  // exactly zero weight
+  auto mask_and_rescale = [&](int j0, f32x16 (&sc)[RG][NH]) {
+    if ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw)) {
 #pragma unroll
       for (int r = 0; r < RG; ++r)
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            f32x8 e8;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
-            pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
-            // row sum of the rounded probabilities actually used below
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
-              l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
-            }
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+            bool ok = key < kend;
+            if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
+            sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
           }
-      const char* v_cur = vbuf(std::integral_constant<int, u>{});
+    }
+    float m_tile[RG];
+    bool grow = false;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      float mx = sc[r][0][0];
 #pragma unroll
       for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[r][hh][e]);
+      m_tile[r] = pair_max(mx) * cs;                 // -inf if the row has no key here
+      grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-          for (int i = 0; i < NO; ++i) {
-            const char* vb = v_cur + (32 * hh + 16 * m) * ROWB + v_rd[i];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
-            const bf16x8 vf =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int r = 0; r < RG; ++r) {
+        const float m_new = fmaxf(m_run[r], m_tile[r]);
+        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);   // 0 when m_run = -inf
+        m_run[r] = m_new;
+        base[r] = b_new;
+        l_run[r] *= alpha;
 #pragma unroll
-            for (int r = 0; r < RG; ++r)
-              acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[r][hh][m], acc[r][i], 0, 0, 0);
+        for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
+      }
+    }
+  };
+  // probabilities rounded to bf16 (P operand) and their row sum
+  auto probabilities = [&](const f32x16 (&sc)[RG][NH], bf16x8 (&pk)[RG][NH][2]) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          f32x8 e8;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
+          pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
+          // row sum of the rounded probabilities actually used in O^T += V^T P^T
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
+            l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
           }
-    }
-    // The next step reads K(it+2) and V(it+1), loaded by step it+2-NBUF:
-    // only the loads of the NBUF-2 most recent steps may stay in flight.
-    int batches = 0;
+        }
+  };
+  // O^T += V^T P^T over one V tile
+  auto pv = [&](const char* v_cur, const bf16x8 (&pk)[RG][NH][2]) {
 #pragma unroll
-    for (int k = 0; k < NBUF - 2; ++k) {
-      const int sk = it - k;
-      if (sk >= 0) batches += (sk + NBUF < ntiles) + (sk + NBUF - 1 < ntiles);
-    }
-    static_for<0, 2 * (NBUF - 2) + 1>([&](auto N) {
-      if (batches == N) pipeline_barrier<N * NLD>();
-    });
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < NO; ++i) {
+          const char* vb = v_cur + (32 * hh + 16 * m) * ROWB + v_rd[i];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
+          const bf16x8 vf =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int r = 0; r < RG; ++r)
+            acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[r][hh][m], acc[r][i], 0, 0, 0);
+        }
   };
 
-  // prologue: K(0 .. NBUF-1) and V(0 .. NBUF-2), then the scores of tile 0
-  static_for<0, NBUF>([&](auto I) {
-    if (I < ntiles) load_k(I * BN, kbuf(I));
-  });
-  static_for<0, NBUF - 1>([&](auto I) {
-    if (I < ntiles) load_v(I * BN, vbuf(I));
-  });
-  pipeline_barrier<0>();
-  if (ntw > 0) scores(kb0, s2[0]);
-  pipeline_barrier<0>();             // K(0) consumed: its buffer takes K(NBUF)
-  for (int it0 = 0; it0 < ntiles; it0 += UNR) {
-    static_for<0, UNR>([&](auto U) {
-      if (it0 + U < ntiles) step(it0 + U, U);
+  if constexpr (PIPE) {
+    // Software pipeline, one BN-key tile per step: the matrix cores compute
+    // the scores of tile j+1 while the vector ALUs turn the scores of tile j
+    // into probabilities, then O^T += V^T P^T for tile j.  K is therefore
+    // staged one tile ahead of V: step j reads K(j+1) and V(j) and prefetches
+    // K(j+NBUF) and V(j+NBUF-1).
+    f32x16 s2[2][RG][NH];
+    auto step = [&](int it, auto U) {
+      constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
+      f32x16 (&sc)[RG][NH] = s2[u & 1];
+      f32x16 (&sn)[RG][NH] = s2[(u + 1) & 1];
+      const int j0 = it * BN;
+      if (it + NBUF < ntiles) load_k(j0 + NBUF * BN, kbuf(std::integral_constant<int, u>{}));
+      if (it + NBUF - 1 < ntiles)
+        load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
+      if (it < ntw) {
+        mask_and_rescale(j0, sc);
+        // scores of the next tile (unused past the wave's last tile)
+        scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+        bf16x8 pk[RG][NH][2];
+        probabilities(sc, pk);
+        pv(vbuf(std::integral_constant<int, u>{}), pk);
+      }
+      // The next step reads K(it+2) and V(it+1), loaded by step it+2-NBUF:
+      // only the loads of the NBUF-2 most recent steps may stay in flight.
+      int batches = 0;
+#pragma unroll
+      for (int k = 0; k < NBUF - 2; ++k) {
+        const int sk = it - k;
+        if (sk >= 0) batches += (sk + NBUF < ntiles) + (sk + NBUF - 1 < ntiles);
+      }
+      static_for<0, 2 * (NBUF - 2) + 1>([&](auto N) {
+        if (batches == N) pipeline_barrier<N * NLD>();
+      });
+    };
+
+    // prologue: K(0 .. NBUF-1) and V(0 .. NBUF-2), then the scores of tile 0
+    static_for<0, NBUF>([&](auto I) {
+      if (I < ntiles) load_k(I * BN, kbuf(I));
     });
+    static_for<0, NBUF - 1>([&](auto I) {
+      if (I < ntiles) load_v(I * BN, vbuf(I));
+    });
+    pipeline_barrier<0>();
+    if (ntw > 0) scores(kb0, s2[0]);
+    pipeline_barrier<0>();             // K(0) consumed: its buffer takes K(NBUF)
+    for (int it0 = 0; it0 < ntiles; it0 += UNR) {
+      static_for<0, UNR>([&](auto U) {
+        if (it0 + U < ntiles) step(it0 + U, U);
+      });
+    }
+  } else {
+    // One tile per step in sequence (scores, softmax, PV); K(j+1) and V(j+1)
+    // load into the other buffers meanwhile.
+    auto step = [&](int it, auto U) {
+      constexpr int u = decltype(U)::value;
+      const int j0 = it * BN;
+      if (it + 1 < ntiles) {
+        load_k(j0 + BN, kbuf(std::integral_constant<int, u + 1>{}));
+        load_v(j0 + BN, vbuf(std::integral_constant<int, u + 1>{}));
+      }
+      if (it < ntw) {
+        f32x16 sc[RG][NH];
+        scores(kbuf(std::integral_constant<int, u>{}), sc);
+        mask_and_rescale(j0, sc);
+        bf16x8 pk[RG][NH][2];
+        probabilities(sc, pk);
+        pv(vbuf(std::integral_constant<int, u>{}), pk);
+      }
+      pipeline_barrier<0>();
+    };
+    if (ntiles > 0) {
+      load_k(0, kb0);
+      load_v(0, vb0);
+    }
+    pipeline_barrier<0>();
+    for (int it0 = 0; it0 < ntiles; it0 += 2) {
+      static_for<0, 2>([&](auto U) {
+        if (it0 + U < ntiles) step(it0 + U, U);
+      });
+    }
   }
 
   // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane ----
