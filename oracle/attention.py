@@ -42,7 +42,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["allowed_mask", "attention_fp64", "softmax_rows_fp64"]
+__all__ = ["allowed_mask", "attention_backward_fp64", "attention_fp64", "attention_lse_fp64",
+           "softmax_rows_fp64"]
 
 
 def allowed_mask(rows: np.ndarray, Tk: int, causal: bool, key_len: int | None) -> np.ndarray:
@@ -120,3 +121,85 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None,
             if return_weights:
                 wts[b, hh, r0:r0 + block] = w
     return (out, wts) if return_weights else out
+
+
+def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None, block: int = 256):
+    """Attention output plus the per-row log-sum-exp of the scaled scores, fp64.
+
+    lse[b, h, i] = log sum_{j allowed} exp(scale * q_i . k_j)   (natural log),
+    -inf for a row with no allowed key.  This is the normaliser of the row
+    softmax (overview page, stable softmax: the row sum of exp) kept in log
+    form, so that the weights can be recomputed as exp(s_ij - lse_i).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, Tq, dk = q.shape
+    Tk = k.shape[2]
+    out = attention_fp64(q, k, v, scale, causal=causal, key_lens=key_lens, block=block)
+    lse = np.full((B, H, Tq), -np.inf, dtype=np.float64)
+    sc = float(scale)
+    for b in range(B):
+        L = None if key_lens is None else int(np.asarray(key_lens)[b])
+        for hh in range(H):
+            kb = k[b, hh].astype(np.float64)
+            for r0 in range(0, Tq, block):
+                ridx = np.arange(r0, min(r0 + block, Tq))
+                s = (q[b, hh, ridx].astype(np.float64) @ kb.T) * sc
+                ok = allowed_mask(ridx, Tk, causal, L)
+                s = np.where(ok, s, -np.inf)
+                any_ok = ok.any(axis=-1)
+                m = np.where(any_ok, s.max(axis=-1, initial=-np.inf), 0.0)
+                with np.errstate(divide="ignore"):
+                    lse[b, hh, ridx] = np.where(any_ok, m + np.log(np.exp(s - m[:, None]).sum(axis=-1)),
+                                                -np.inf)
+    return out, lse
+
+
+def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool = False, key_lens=None):
+    """Gradients of O = softmax(scale * Q K^T) V with respect to Q, K, V, fp64.
+
+    Training the model on the pages means back-propagating a loss through
+    this formula (aiany.app Step 11, cross-entropy training nudging every
+    weight; notebook chapter, "Layer Normalization and Residual Connections",
+    gradients flowing through each sublayer).  With P the row-softmax weights
+    (zero where masked) and dO the gradient of the loss with respect to O, the
+    chain rule through O = P V and the row softmax gives:
+        dV = P^T dO
+        dP = dO V^T
+        D_i = sum_j P_ij dP_ij  (= dO_i . O_i)
+        dS = P * (dP - D)       (elementwise, D broadcast along rows)
+        dQ = scale * dS K,   dK = scale * dS^T Q
+    Rows with no allowed key contribute nothing.  Returns (dq, dk, dv, delta)
+    with delta = D of shape [B, h, Tq].  Whole score matrices per (b, head):
+    for test sizes only.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout)
+    B, H, Tq, dk = q.shape
+    Tk = k.shape[2]
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dkk = np.zeros(k.shape, dtype=np.float64)
+    dvv = np.zeros(v.shape, dtype=np.float64)
+    delta = np.zeros((B, H, Tq), dtype=np.float64)
+    sc = float(scale)
+    rows = np.arange(Tq)
+    for b in range(B):
+        L = None if key_lens is None else int(np.asarray(key_lens)[b])
+        ok = allowed_mask(rows, Tk, causal, L)
+        for hh in range(H):
+            qb = q[b, hh].astype(np.float64)
+            kb = k[b, hh].astype(np.float64)
+            vb = v[b, hh].astype(np.float64)
+            gb = dout[b, hh].astype(np.float64)
+            p = softmax_rows_fp64((qb @ kb.T) * sc, ok)
+            dvv[b, hh] = p.T @ gb
+            dp = gb @ vb.T
+            d_row = (p * dp).sum(axis=-1)
+            ds = p * (dp - d_row[:, None])
+            dq[b, hh] = sc * (ds @ kb)
+            dkk[b, hh] = sc * (ds.T @ qb)
+            delta[b, hh] = d_row
+    return dq, dkk, dvv, delta
