@@ -70,10 +70,12 @@ enum {
   ATTN_ERR_SHAPE = -2,       /* negative dimension, or d_k != d_v */
   ATTN_ERR_HEADDIM = -3,     /* head size not supported (supported: 64, 128) */
   ATTN_ERR_MASK = -4,        /* unknown mask bits, or KEYPAD with key_lens == NULL */
-  ATTN_ERR_ALIAS = -5,       /* out overlaps q, k or v */
-  ATTN_ERR_ALIGN = -6,       /* q, k, v or out not 16-byte aligned; key_lens not 4-byte aligned */
+  ATTN_ERR_ALIAS = -5,       /* an output buffer overlaps an input or another output */
+  ATTN_ERR_ALIGN = -6,       /* a bf16/fp32 tensor not 16-byte aligned; key_lens, lse or delta
+                                not 4-byte aligned */
   ATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
-  ATTN_ERR_TOO_LARGE = -8,   /* B*h*ceil(Tq/128) work-groups exceed the launch limit */
+  ATTN_ERR_TOO_LARGE = -8,   /* more than 2^31-1 work-groups, or one head's rows of a tensor
+                                exceed 4 GiB (T * d * element size >= 2^32) */
   ATTN_ERR_HIP = -100        /* the kernel launch failed; see attn_last_hip_error() */
 };
 
@@ -103,6 +105,59 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out,
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* out,
                  int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
                  int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
+ * attn_fwd_lse: attn_fwd (bfloat16, same arguments and semantics) that also
+ * writes the log-sum-exp of every query row's scaled, allowed scores,
+ *
+ *     lse[b,h,i] = ln sum_{j allowed} exp(s_ij)     (natural log, fp32),
+ *
+ * -inf for a row with no allowed key.  It is the normaliser of the row
+ * softmax (the row sum of exp in the stable softmax of the azimuth.plus
+ * overview, "The idea: every word queries every word") kept in log form:
+ * w_ij = exp(s_ij - lse_i), which is what attn_bwd recomputes the weights
+ * from.  The value is the normaliser the kernel actually divided by (its sum
+ * of the bfloat16-rounded probabilities).
+ *   lse : device fp32 [B, h, Tq], 4-byte aligned, caller-owned, must not
+ *         overlap q, k, v or out; NULL is ATTN_ERR_NULL unless the work is empty.
+ */
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
+                 int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
+ * attn_bwd: gradients of out = attention(q, k, v) (the operation above, same
+ * scale and mask) with respect to q, k and v, given the gradient dout of a
+ * loss with respect to out.  Training through the formula is what the pages
+ * describe (aiany.app explainer, Step 11: every weight matrix is nudged by
+ * back-propagating a cross-entropy loss).  With w the weights and
+ * D_i = <dout_i, out_i>, the chain rule through out = w v and the row softmax:
+ *
+ *     dv_j = sum_i w_ij dout_i
+ *     dp_ij = <dout_i, v_j>,   ds_ij = w_ij (dp_ij - D_i)
+ *     dq_i = scale sum_j ds_ij k_j,   dk_j = scale sum_i ds_ij q_i
+ *
+ * Keys that no query row may see (past L_b, or beyond every row under the
+ * causal mask) get zero dk and dv; rows with no allowed key get zero dq.
+ *   q, k, v, out, dout : bfloat16 inputs, layout above; out and lse are what
+ *                        attn_fwd_lse returned for these q, k, v, scale, mask
+ *   lse                : fp32 [B, h, Tq] from attn_fwd_lse
+ *   delta              : fp32 [B, h, Tq] caller-owned workspace; written with
+ *                        D_i (computed from the bfloat16 out and dout)
+ *   dq, dk, dv         : bfloat16 outputs shaped like q, k, v (fp32
+ *                        accumulation, one rounding each)
+ *   other arguments    : as for attn_fwd; d_k = d_v in {64, 128}
+ * Two kernels are enqueued on `stream`: the first writes delta and dq, the
+ * second reads delta and writes dk, dv.  Outputs may not overlap any input
+ * or each other (ATTN_ERR_ALIAS).  Empty work: B or h = 0, or Tq = Tk = 0,
+ * is a no-op; Tq = 0 with Tk > 0 writes zero dk, dv (q, out, dout, lse,
+ * delta, dq unused); Tk = 0 with Tq > 0 writes zero dq and delta (k, v, dk,
+ * dv unused).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv,
+             int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
+             int mask_kind, const int32_t* key_lens, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_str(int status);

@@ -42,8 +42,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["allowed_mask", "attention_backward_fp64", "attention_fp64", "attention_lse_fp64",
-           "softmax_rows_fp64"]
+__all__ = ["allowed_mask", "attention_backward_fp64", "attention_backward_sampled_fp64", "attention_fp64",
+           "attention_lse_fp64", "softmax_rows_fp64"]
 
 
 def allowed_mask(rows: np.ndarray, Tk: int, causal: bool, key_len: int | None) -> np.ndarray:
@@ -123,36 +123,41 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None,
     return (out, wts) if return_weights else out
 
 
-def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None, block: int = 256):
+def attention_lse_fp64(q, k, v, scale: float, causal: bool = False, key_lens=None, block: int = 256,
+                       rows=None):
     """Attention output plus the per-row log-sum-exp of the scaled scores, fp64.
 
     lse[b, h, i] = log sum_{j allowed} exp(scale * q_i . k_j)   (natural log),
     -inf for a row with no allowed key.  This is the normaliser of the row
     softmax (overview page, stable softmax: the row sum of exp) kept in log
     form, so that the weights can be recomputed as exp(s_ij - lse_i).
+    rows: None (all query rows) or a 1-D index array: out and lse are then
+    [B, h, len(rows), ...] for those rows only.
     """
     q = np.asarray(q)
     k = np.asarray(k)
     v = np.asarray(v)
     B, H, Tq, dk = q.shape
     Tk = k.shape[2]
-    out = attention_fp64(q, k, v, scale, causal=causal, key_lens=key_lens, block=block)
-    lse = np.full((B, H, Tq), -np.inf, dtype=np.float64)
+    row_idx = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = row_idx.shape[0]
+    out = attention_fp64(q, k, v, scale, causal=causal, key_lens=key_lens, rows=rows, block=block)
+    lse = np.full((B, H, R), -np.inf, dtype=np.float64)
     sc = float(scale)
     for b in range(B):
         L = None if key_lens is None else int(np.asarray(key_lens)[b])
         for hh in range(H):
             kb = k[b, hh].astype(np.float64)
-            for r0 in range(0, Tq, block):
-                ridx = np.arange(r0, min(r0 + block, Tq))
+            for r0 in range(0, R, block):
+                ridx = row_idx[r0:r0 + block]
                 s = (q[b, hh, ridx].astype(np.float64) @ kb.T) * sc
                 ok = allowed_mask(ridx, Tk, causal, L)
                 s = np.where(ok, s, -np.inf)
                 any_ok = ok.any(axis=-1)
                 m = np.where(any_ok, s.max(axis=-1, initial=-np.inf), 0.0)
                 with np.errstate(divide="ignore"):
-                    lse[b, hh, ridx] = np.where(any_ok, m + np.log(np.exp(s - m[:, None]).sum(axis=-1)),
-                                                -np.inf)
+                    lse[b, hh, r0:r0 + block] = np.where(
+                        any_ok, m + np.log(np.exp(s - m[:, None]).sum(axis=-1)), -np.inf)
     return out, lse
 
 
@@ -203,3 +208,58 @@ def attention_backward_fp64(q, k, v, dout, scale: float, causal: bool = False, k
             dkk[b, hh] = sc * (ds.T @ qb)
             delta[b, hh] = d_row
     return dq, dkk, dvv, delta
+
+
+def attention_backward_sampled_fp64(q, k, v, dout, scale: float, causal: bool = False, key_lens=None,
+                                    rows=None, keys=None, heads=None, block: int = 256):
+    """The gradients of attention_backward_fp64 at a subset of positions, fp64.
+
+    dq at query rows `rows` and dk, dv at key positions `keys` (1-D index
+    arrays, None = none), for the (b, head) pairs in `heads` (None = all).
+    Same formulas; the score matrix is never held whole:
+      * dq_i needs only row i of P and dP: dS_i = P_i * (dP_i - D_i),
+        dq_i = scale * dS_i K;
+      * dk_j, dv_j need column j of P and dP over every row, and D_i for every
+        row, so all rows are swept in blocks of `block`, each block taking its
+        full rows of P (two-pass softmax) and dP, and contributing
+        dv_j += P_bj^T dO_b and dk_j += scale * dS_bj^T Q_b.
+    Returns (dq [B, h, len(rows), d], dk [B, h, len(keys), d], dv [...]);
+    pairs not selected are left 0.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    dout = np.asarray(dout)
+    B, H, Tq, dk_ = q.shape
+    Tk = k.shape[2]
+    dv_ = v.shape[3]
+    rows = np.zeros(0, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    keys = np.zeros(0, dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64)
+    gq = np.zeros((B, H, rows.shape[0], dk_))
+    gk = np.zeros((B, H, keys.shape[0], dk_))
+    gv = np.zeros((B, H, keys.shape[0], dv_))
+    pairs = [(b, hh) for b in range(B) for hh in range(H)] if heads is None else list(heads)
+    sc = float(scale)
+    for b, hh in pairs:
+        L = None if key_lens is None else int(np.asarray(key_lens)[b])
+        kb = k[b, hh].astype(np.float64)
+        vb = v[b, hh].astype(np.float64)
+        if rows.shape[0]:
+            qr = q[b, hh, rows].astype(np.float64)
+            gr = dout[b, hh, rows].astype(np.float64)
+            p = softmax_rows_fp64((qr @ kb.T) * sc, allowed_mask(rows, Tk, causal, L))
+            dp = gr @ vb.T
+            ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+            gq[b, hh] = sc * (ds @ kb)
+        if keys.shape[0]:
+            for r0 in range(0, Tq, block):
+                ridx = np.arange(r0, min(r0 + block, Tq))
+                qb = q[b, hh, ridx].astype(np.float64)
+                gb = dout[b, hh, ridx].astype(np.float64)
+                p = softmax_rows_fp64((qb @ kb.T) * sc, allowed_mask(ridx, Tk, causal, L))
+                dp = gb @ vb.T
+                d_row = (p * dp).sum(axis=-1, keepdims=True)
+                pc = p[:, keys]
+                gv[b, hh] += pc.T @ gb
+                gk[b, hh] += sc * ((pc * (dp[:, keys] - d_row)).T @ qb)
+    return gq, gk, gv

@@ -39,7 +39,8 @@ def _declared_enum():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["attn_fwd", "attn_fwd_f32", "attn_status_str", "attn_last_hip_error", "attn_version"])
+        ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_bwd", "attn_status_str", "attn_last_hip_error",
+         "attn_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -113,6 +114,7 @@ def _call(L, f32=False, **over):
     (dict(out=K + 4096), "ERR_ALIAS"),
     (dict(out=V - 16), "ERR_ALIAS"),
     (dict(B=1 << 30, h=1 << 10, Tq=1 << 20), "ERR_TOO_LARGE"),
+    (dict(B=1, h=1, Tk=1 << 25, d_k=128, d_v=128), "ERR_TOO_LARGE"),   # one head's K: 8 GiB
 ])
 def test_bad_arguments_rejected_before_any_launch(L, f32, over, code):
     assert _call(L, f32=f32, **over) == getattr(L, code)
@@ -127,6 +129,97 @@ def test_empty_problem_is_a_no_op(L, over):
 
 def test_keypad_needs_key_lens_even_when_empty(L):
     assert _call(L, B=0, mask_kind=L.MASK_KEYPAD) == L.ERR_MASK
+
+
+LSE = 0x60000000
+
+
+def _call_lse(L, **over):
+    a = dict(GOOD, lse=LSE)
+    a.update(over)
+    return L.attn_fwd_lse(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["h"], a["Tq"], a["Tk"],
+                          a["d_k"], a["d_v"], a["scale"], a["mask_kind"], a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(lse=None), "ERR_NULL"),
+    (dict(lse=LSE + 2), "ERR_ALIGN"),
+    (dict(lse=O + 64), "ERR_ALIAS"),
+    (dict(lse=Q), "ERR_ALIAS"),
+    (dict(d_k=32, d_v=32), "ERR_HEADDIM"),
+    (dict(mask_kind=2), "ERR_MASK"),
+    (dict(scale=float("nan")), "ERR_SCALE"),
+    (dict(out=K), "ERR_ALIAS"),
+])
+def test_fwd_lse_bad_arguments(L, over, code):
+    assert _call_lse(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+def test_fwd_lse_empty_is_a_no_op(L):
+    assert _call_lse(L, Tq=0, lse=None) == L.OK
+    assert _call_lse(L, B=0, lse=None, q=None, out=None) == L.OK
+
+
+# backward: fake addresses 256 MiB apart, never dereferenced
+BW = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, dout=0x50000000, lse=0x60000000,
+          delta=0x70000000, dq=0x80000000, dk=0x90000000, dv=0xA0000000, B=2, h=3, Tq=70, Tk=90, d_k=64,
+          d_v=64, scale=0.125, mask_kind=0, key_lens=None, stream=None)
+
+
+def _call_bwd(L, **over):
+    a = dict(BW)
+    a.update(over)
+    return L.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["delta"], a["dq"], a["dk"],
+                      a["dv"], a["B"], a["h"], a["Tq"], a["Tk"], a["d_k"], a["d_v"], a["scale"],
+                      a["mask_kind"], a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "ERR_SHAPE"),
+    (dict(Tk=-3), "ERR_SHAPE"),
+    (dict(d_v=128), "ERR_SHAPE"),
+    (dict(d_k=96, d_v=96), "ERR_HEADDIM"),
+    (dict(mask_kind=8), "ERR_MASK"),
+    (dict(mask_kind=2), "ERR_MASK"),
+    (dict(scale=float("inf")), "ERR_SCALE"),
+    (dict(q=None), "ERR_NULL"),
+    (dict(out=None), "ERR_NULL"),
+    (dict(dout=None), "ERR_NULL"),
+    (dict(lse=None), "ERR_NULL"),
+    (dict(delta=None), "ERR_NULL"),
+    (dict(dq=None), "ERR_NULL"),
+    (dict(k=None), "ERR_NULL"),
+    (dict(v=None), "ERR_NULL"),
+    (dict(dk=None), "ERR_NULL"),
+    (dict(dv=None), "ERR_NULL"),
+    (dict(Tq=0, dk=None), "ERR_NULL"),          # the dK/dV kernel still runs
+    (dict(Tk=0, dq=None), "ERR_NULL"),          # the dQ kernel still runs
+    (dict(dout=0x50000008), "ERR_ALIGN"),
+    (dict(dq=0x80000004), "ERR_ALIGN"),
+    (dict(dk=0x90000002), "ERR_ALIGN"),
+    (dict(dv=0xA0000008), "ERR_ALIGN"),
+    (dict(lse=0x60000002), "ERR_ALIGN"),
+    (dict(delta=0x70000001), "ERR_ALIGN"),
+    (dict(mask_kind=2, key_lens=0xB0000002), "ERR_ALIGN"),
+    (dict(dq=0x10000000 + 4096), "ERR_ALIAS"),  # dq inside q
+    (dict(dk=0x80000000 + 64), "ERR_ALIAS"),    # dk inside dq
+    (dict(delta=0x60000000 + 16), "ERR_ALIAS"), # delta inside lse
+    (dict(dv=0x50000000), "ERR_ALIAS"),         # dv on dout
+    (dict(delta=0xA0000000 + 128), "ERR_ALIAS"),
+    (dict(B=1 << 30, h=1 << 10, Tq=1 << 20), "ERR_TOO_LARGE"),
+    (dict(B=1, h=1, Tq=1 << 24, d_k=128, d_v=128), "ERR_TOO_LARGE"),   # one head's Q: 4 GiB
+])
+def test_bwd_bad_arguments_rejected_before_any_launch(L, over, code):
+    assert _call_bwd(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(h=0), dict(Tq=0, Tk=0),
+                                  dict(B=0, **{n: None for n in ("q", "k", "v", "out", "dout", "lse", "delta",
+                                                                 "dq", "dk", "dv")})])
+def test_bwd_empty_problem_is_a_no_op(L, over):
+    assert _call_bwd(L, **over) == L.OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -16,7 +16,7 @@ import pytest
 from scipy.special import logsumexp
 
 import oracle
-from oracle import attention_backward_fp64, attention_fp64, attention_lse_fp64
+from oracle import attention_backward_fp64, attention_backward_sampled_fp64, attention_fp64, attention_lse_fp64
 
 
 def _rand(shape, seed, scale=1.0):
@@ -125,6 +125,12 @@ def test_lse_matches_scipy_logsumexp_and_closed_forms():
     np.testing.assert_allclose(lse[0, 0], 2.0 * (qq[0, 0] @ kk[0, 0, 0]), atol=1e-14)
     _, lse = attention_lse_fp64(qq, kk, kk, 2.0, key_lens=[0])
     assert np.all(lse == -np.inf)
+    # a row subset gives the same rows as the full computation
+    out_f, lse_f = attention_lse_fp64(q, k, v, 0.45, causal=True, key_lens=[9, 4], block=3)
+    rows = np.array([0, 4, 6])
+    out_r, lse_r = attention_lse_fp64(q, k, v, 0.45, causal=True, key_lens=[9, 4], rows=rows, block=2)
+    np.testing.assert_allclose(lse_r, lse_f[:, :, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out_r, out_f[:, :, rows], rtol=0, atol=1e-14)
 
 
 @pytest.mark.parametrize("kind", ["no_scale", "sign", "delta_from_dp", "no_transpose"])
@@ -148,3 +154,24 @@ def test_planted_gradient_mistakes_fail_finite_differences(kind, monkeypatch):
     ok = (np.allclose(dq, _fd_grad(f, q), atol=1e-6) and np.allclose(dk, _fd_grad(f, k), atol=1e-6)
           and np.allclose(dv, _fd_grad(f, v), atol=1e-6))
     assert not ok
+
+
+@pytest.mark.parametrize("causal,key_lens", [(False, None), (True, None), (False, [40, 0]), (True, [70, 13])])
+def test_sampled_gradients_equal_the_full_ones(causal, key_lens):
+    """The blocked, sampled form (for long sequences) reduces to the whole-matrix one, which the
+    finite-difference and autograd pins above fix."""
+    B, H, Tq, Tk, d = 2, 2, 75, 83, 5
+    q, k, v, g = _rand((B, H, Tq, d), 40), _rand((B, H, Tk, d), 41), _rand((B, H, Tk, d), 42), _rand((B, H, Tq, d), 43)
+    dq, dk, dv, _ = attention_backward_fp64(q, k, v, g, 0.6, causal=causal, key_lens=key_lens)
+    rows = np.array([0, 3, 31, 32, 74])
+    keys = np.array([0, 1, 12, 39, 40, 69, 82])
+    sq, sk, sv = attention_backward_sampled_fp64(q, k, v, g, 0.6, causal=causal, key_lens=key_lens, rows=rows,
+                                                 keys=keys, block=16)
+    np.testing.assert_allclose(sq, dq[:, :, rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sk, dk[:, :, keys], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sv, dv[:, :, keys], rtol=0, atol=1e-12)
+    # a head subset leaves the others zero
+    sq, sk, _ = attention_backward_sampled_fp64(q, k, v, g, 0.6, causal=causal, key_lens=key_lens, rows=rows,
+                                                keys=keys, heads=[(1, 0)])
+    np.testing.assert_allclose(sq[1, 0], dq[1, 0, rows], rtol=0, atol=1e-12)
+    assert not sq[0].any() and not sk[0].any() and not sq[1, 1].any()

@@ -32,9 +32,13 @@ ERR_HIP = -100
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _FWD_ARGS = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P]
+_FWD_LSE_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P]
+_BWD_ARGS = [_P] * 10 + [_I] * 6 + [ctypes.c_float, _I, _P, _P]
 SIGNATURES = {
     "attn_fwd": (_I, _FWD_ARGS),
     "attn_fwd_f32": (_I, _FWD_ARGS),
+    "attn_fwd_lse": (_I, _FWD_LSE_ARGS),
+    "attn_bwd": (_I, _BWD_ARGS),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
     "attn_version": (ctypes.c_char_p, []),
@@ -78,6 +82,19 @@ def attn_fwd_f32(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_len
     """fp32 attention forward (attn.h `attn_fwd_f32`)."""
     return raw_library().attn_fwd_f32(q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
                                       stream)
+
+
+def attn_fwd_lse(q, k, v, out, lse, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream) -> int:
+    """bf16 attention forward that also writes the fp32 row log-sum-exp (attn.h `attn_fwd_lse`)."""
+    return raw_library().attn_fwd_lse(q, k, v, out, lse, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+                                      stream)
+
+
+def attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+             stream) -> int:
+    """bf16 attention backward: dq, dk, dv (and delta) from out, dout and lse (attn.h `attn_bwd`)."""
+    return raw_library().attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v, scale,
+                                  mask_kind, key_lens, stream)
 
 
 def attn_status_str(status: int) -> str:

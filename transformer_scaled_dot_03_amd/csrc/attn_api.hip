@@ -23,8 +23,15 @@ bool overlaps(const void* a, unsigned __int128 na, const void* b, unsigned __int
 
 bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
-int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, int B, int h, int Tq,
-        int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
+// |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always map to
+// exp2(-inf) = 0; for scale = 0 every exp2 argument then rounds to 0 and the
+// weights are exactly uniform, as for a true zero.
+float scale_log2(float scale) {
+  return static_cast<float>(std::fmax(std::fabs(static_cast<double>(scale)) * 1.4426950408889634, 1e-30));
+}
+
+int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, float* lse, int B, int h,
+        int Tq, int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
         hipStream_t stream) {
   if (B < 0 || h < 0 || Tq < 0 || Tk < 0 || d_k < 0 || d_v < 0) return ATTN_ERR_SHAPE;
   if (d_k != d_v) return ATTN_ERR_SHAPE;
@@ -40,18 +47,27 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
   if (misaligned(q, 16) || misaligned(out, 16) || (Tk > 0 && (misaligned(k, 16) || misaligned(v, 16))))
     return ATTN_ERR_ALIGN;
   if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
+  if (lse != nullptr && misaligned(lse, 4)) return ATTN_ERR_ALIGN;
 
   const int64_t bm = attn::rows_per_block(dt, d_k);
   const int64_t bh = static_cast<int64_t>(B) * h;
   const int64_t n_qtiles = (Tq + bm - 1) / bm;
   const int64_t n_wg = bh * n_qtiles;  // B, h < 2^31 and n_qtiles < 2^25: no overflow
   if (n_wg > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  // the kernels address one head's K / V rows through a buffer descriptor with a 32-bit byte range
+  if (static_cast<int64_t>(Tk) * d_k * (dt == attn::DType::F32 ? 4 : 2) > 0xffffffffLL) return ATTN_ERR_TOO_LARGE;
 
   typedef unsigned __int128 u128;
   const u128 es = dt == attn::DType::F32 ? 4 : 2;
   const u128 nq = (u128)bh * Tq * d_k * es, nkv = (u128)bh * Tk * d_k * es, no = (u128)bh * Tq * d_v * es;
   if (overlaps(out, no, q, nq) || overlaps(out, no, k, nkv) || overlaps(out, no, v, nkv))
     return ATTN_ERR_ALIAS;
+  if (lse != nullptr) {
+    const u128 nl = (u128)bh * Tq * 4;
+    if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+        overlaps(lse, nl, out, no))
+      return ATTN_ERR_ALIAS;
+  }
 
   attn::Params p;
   p.q = q;
@@ -63,14 +79,90 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
   p.H = h;
   p.Tq = Tq;
   p.Tk = Tk;
-  // |scale| * log2(e), kept >= 1e-30 so that masked (-inf) scores always map to
-  // exp2(-inf) = 0; for scale = 0 every exp2 argument then rounds to 0 and the
-  // weights are exactly uniform, as for a true zero.
-  p.scale_log2 = static_cast<float>(std::fmax(std::fabs(static_cast<double>(scale)) * 1.4426950408889634, 1e-30));
+  p.scale_log2 = scale_log2(scale);
   p.neg = scale < 0.f ? 1 : 0;
   p.n_qtiles = static_cast<int>(n_qtiles);
   p.n_wg = static_cast<int>(n_wg);
+  p.lse = lse;
   const hipError_t e = attn::launch_fwd(p, dt, d_k, causal, keypad, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+int bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+        float* delta, void* dq, void* dk, void* dv, int B, int h, int Tq, int Tk, int d_k, int d_v,
+        float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
+  if (B < 0 || h < 0 || Tq < 0 || Tk < 0 || d_k < 0 || d_v < 0) return ATTN_ERR_SHAPE;
+  if (d_k != d_v) return ATTN_ERR_SHAPE;
+  if (d_k != 64 && d_k != 128) return ATTN_ERR_HEADDIM;
+  if (mask_kind & ~(ATTN_MASK_CAUSAL | ATTN_MASK_KEYPAD)) return ATTN_ERR_MASK;
+  const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
+  const bool keypad = (mask_kind & ATTN_MASK_KEYPAD) != 0;
+  if (keypad && key_lens == nullptr) return ATTN_ERR_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || h == 0 || (Tq == 0 && Tk == 0)) return ATTN_OK;  // nothing to write
+  // pointers the launched kernels touch: Tq > 0 runs the dQ kernel (q, out,
+  // dout, lse, delta, dq; k and v when Tk > 0), Tk > 0 the dK/dV kernel (k, v,
+  // dk, dv; q, dout, lse, delta when Tq > 0)
+  const bool rows = Tq > 0, keys = Tk > 0;
+  if (rows && (q == nullptr || out == nullptr || dout == nullptr || lse == nullptr || delta == nullptr ||
+               dq == nullptr))
+    return ATTN_ERR_NULL;
+  if (keys && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return ATTN_ERR_NULL;
+  if (rows && (misaligned(q, 16) || misaligned(out, 16) || misaligned(dout, 16) || misaligned(dq, 16) ||
+               misaligned(lse, 4) || misaligned(delta, 4)))
+    return ATTN_ERR_ALIGN;
+  if (keys && (misaligned(k, 16) || misaligned(v, 16) || misaligned(dk, 16) || misaligned(dv, 16)))
+    return ATTN_ERR_ALIGN;
+  if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
+
+  const int64_t bh = static_cast<int64_t>(B) * h;
+  const int64_t bm = attn::bwd_rows_per_block(d_k), bn = attn::bwd_keys_per_block(d_k);
+  const int64_t n_qtiles = (Tq + bm - 1) / bm, n_ktiles = (Tk + bn - 1) / bn;
+  if (bh * n_qtiles > 0x7fffffffLL || bh * n_ktiles > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  // one head's rows (K, V in the dQ kernel; Q, dO in the dK/dV kernel) sit behind a 32-bit byte range
+  if (static_cast<int64_t>(Tq > Tk ? Tq : Tk) * d_k * 2 > 0xffffffffLL) return ATTN_ERR_TOO_LARGE;
+
+  // written: delta, dq (rows), dk, dv (keys); read: q, k, v, out, dout, lse
+  typedef unsigned __int128 u128;
+  const u128 nq = rows ? (u128)bh * Tq * d_k * 2 : 0, nkv = keys ? (u128)bh * Tk * d_k * 2 : 0;
+  const u128 nr = rows ? (u128)bh * Tq * 4 : 0;
+  const void* in_p[6] = {q, k, v, out, dout, lse};
+  const u128 in_n[6] = {nq, nkv, nkv, nq, nq, nr};
+  const void* out_p[4] = {delta, dq, dk, dv};
+  const u128 out_n[4] = {nr, nq, nkv, nkv};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return ATTN_ERR_ALIAS;
+  }
+
+  attn::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = out;
+  p.dout = dout;
+  p.lse = lse;
+  p.delta = delta;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.key_lens = keypad ? key_lens : nullptr;
+  p.B = B;
+  p.H = h;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.scale_log2 = scale_log2(scale);
+  p.scale = scale;
+  p.neg = scale < 0.f ? 1 : 0;
+  p.n_qtiles = static_cast<int>(n_qtiles);
+  p.n_ktiles = static_cast<int>(n_ktiles);
+  const hipError_t e = attn::launch_bwd(p, d_k, causal, keypad, stream);
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
     return ATTN_ERR_HIP;
@@ -84,13 +176,30 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int h, int Tq, int Tk,
              int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
-  return fwd(attn::DType::BF16, q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream);
+  return fwd(attn::DType::BF16, q, k, v, out, nullptr, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+             stream);
+}
+
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int h, int Tq,
+                 int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
+                 hipStream_t stream) {
+  if (lse == nullptr && B > 0 && h > 0 && Tq > 0) return ATTN_ERR_NULL;
+  return fwd(attn::DType::BF16, q, k, v, out, lse, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+             stream);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             float* delta, void* dq, void* dk, void* dv, int B, int h, int Tq, int Tk, int d_k, int d_v,
+             float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
+  return bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+             stream);
 }
 
 int attn_fwd_f32(const void* q, const void* k, const void* v, void* out, int B, int h, int Tq, int Tk,
                  int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
                  hipStream_t stream) {
-  return fwd(attn::DType::F32, q, k, v, out, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream);
+  return fwd(attn::DType::F32, q, k, v, out, nullptr, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+             stream);
 }
 
 const char* attn_status_str(int status) {
@@ -100,10 +209,10 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_SHAPE: return "bad shape (negative dimension or d_k != d_v)";
     case ATTN_ERR_HEADDIM: return "unsupported head size (supported: 64, 128)";
     case ATTN_ERR_MASK: return "bad mask_kind bits, or key padding without key_lens";
-    case ATTN_ERR_ALIAS: return "out overlaps q, k or v";
-    case ATTN_ERR_ALIGN: return "misaligned pointer (tensors need 16 bytes, key_lens 4)";
+    case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
-    case ATTN_ERR_TOO_LARGE: return "too many work-groups for one launch";
+    case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";
   }

@@ -1,0 +1,438 @@
+// Backward pass of scaled dot-product attention for gfx950 (MI355X):
+// gradients of O = softmax(scale * Q K^T) V with respect to Q, K and V, bf16
+// in and out, fp32 accumulation.
+//
+// With P the row-softmax weights (recomputed as exp(scale s - lse) from the
+// forward's log-sum-exp), dO the incoming gradient and D_i = dO_i . O_i:
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+//     dQ = scale dS K,  dK = scale dS^T Q
+// (chain rule through O = P V and the row softmax; training through the
+// formula is what the pages describe: aiany.app Step 11, cross-entropy
+// training of every weight matrix).
+//
+// Two kernels, no atomics and no scratch beyond the caller's delta array:
+//   * attn_bwd_dq_kernel: one work-group per 128 query rows; writes D_i, then
+//     streams K/V tiles of 64 keys and accumulates dQ in registers;
+//   * attn_bwd_dkdv_kernel: one work-group per 128 keys; streams Q/dO tiles of
+//     64 rows (with their lse and D) and accumulates dK, dV in registers.
+// Matrix-core mapping as in the forward (v_mfma_f32_32x32x16_bf16, lane l,
+// g = l / 32, c = l % 32): products whose output rows are the lane's own
+// row/key take the streamed operand from LDS as 16-byte fragments read in
+// slot order sigma; products contracting over the streamed index take it
+// transposed with ds_read_b64_tr_b16.  Both read patterns share one tile
+// layout (dual_swz) that is free of bank conflicts for both.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBT = 64;            // keys (dQ kernel) or query rows (dK/dV kernel) per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+struct BwdTile {
+  static constexpr int ROWB = D * 2;                       // bytes per row
+  static constexpr int TILEB = kBT * ROWB;                 // bytes per tile
+  static constexpr int NLD = TILEB / 1024 / kBwdWaves;     // 1 KB direct loads per wave
+  static constexpr int DT = D / 16;                        // MFMA steps over d
+  static constexpr int NO = D / 32;                        // 32-column output tiles
+};
+
+// direct-to-LDS source offsets of this lane for a row-major 64-row tile,
+// stored with the dual swizzle
+template <int D>
+__device__ __forceinline__ void tile_src_offsets(int w, int lane, uint32_t (&src)[BwdTile<D>::NLD]) {
+  constexpr int ROWB = BwdTile<D>::ROWB;
+#pragma unroll
+  for (int u = 0; u < BwdTile<D>::NLD; ++u) {
+    const int pos = (kBwdWaves * u + w) * 1024 + 16 * lane;
+    const int r = pos / ROWB, pc = (pos % ROWB) / 16;
+    src[u] = r * ROWB + 16 * (pc ^ dual_swz<D>(r));
+  }
+}
+
+// fragment-read offsets: lane (c, g), step t reads logical chunk 2t + g of row
+// sigma(c) (+ 32 hh rows, an immediate): the A operand of a product whose
+// output rows follow the S^T / S slot order
+template <int D>
+__device__ __forceinline__ void frag_offsets(int c, int g, int (&rd)[BwdTile<D>::DT]) {
+  const int r = sigma32(c);
+#pragma unroll
+  for (int t = 0; t < BwdTile<D>::DT; ++t) rd[t] = r * BwdTile<D>::ROWB + 16 * ((2 * t + g) ^ dual_swz<D>(r));
+}
+
+// transposed-read offsets: in 16-lane group G (h = G & 1, gg = G >> 1) source
+// lane s reads 4 consecutive output columns of row 8gg + 4e + s/4 (+ 16m rows,
+// an immediate); index [i][e] for output tile i and row half e
+template <int D>
+__device__ __forceinline__ void tr_offsets(int lane, int (&rd)[BwdTile<D>::NO][2]) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int h = G & 1, gg = G >> 1;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int r = 8 * gg + 4 * e + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < BwdTile<D>::NO; ++i) {
+      const int lc = (D / 16) * (sl & 1) + 2 * i + h;
+      rd[i][e] = r * BwdTile<D>::ROWB + 16 * (lc ^ dual_swz<D>(r)) + 8 * ((sl >> 1) & 1);
+    }
+  }
+}
+
+// A operand (8 consecutive rows of the transposed tile) from two transposed reads
+__device__ __forceinline__ bf16x8 tr_fragment(const char* lo_addr, const char* hi_addr) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo_addr));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(hi_addr));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// lane's row of a bf16 [., D] matrix in the B-operand layout (d = 16t + 8g + e)
+template <int D>
+__device__ __forceinline__ void load_row(const __bf16* base, int row, int nrows, int g, bool negate,
+                                         bf16x8 (&f)[BwdTile<D>::DT]) {
+  const bool ok = row < nrows;
+  const __bf16* rp = base + (int64_t)(ok ? row : 0) * D + 8 * g;
+#pragma unroll
+  for (int t = 0; t < BwdTile<D>::DT; ++t) {
+    u32x4 x = ok ? *reinterpret_cast<const u32x4*>(rp + 16 * t) : u32x4{0, 0, 0, 0};
+    if (negate) x ^= 0x80008000u;
+    f[t] = __builtin_bit_cast(bf16x8, x);
+  }
+}
+
+// store a lane's accumulated row (columns tau: (D/2) g + 16 i + r) times `mul`
+template <int D>
+__device__ __forceinline__ void store_row(__bf16* base, int row, int g, float mul,
+                                          const f32x16 (&acc)[BwdTile<D>::NO]) {
+  __bf16* op = base + (int64_t)row * D + (D / 2) * g;
+#pragma unroll
+  for (int i = 0; i < BwdTile<D>::NO; ++i)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x8 o8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o8[j] = acc[i][8 * h2 + j] * mul;
+      *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and D) kernel
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool KEYPAD>
+__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
+  using TG = BwdTile<D>;
+  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT, NO = TG::NO;
+  constexpr int BM = 32 * kBwdWaves;
+  constexpr float kNegInf = -__builtin_inff(), kPosInf = __builtin_inff();
+
+  __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  int bh, qt;
+  tile_of_block(p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int q0 = qt * BM, qw = q0 + 32 * w, row = qw + c;
+  int kend = Tk;
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  int kend_wg = CAUSAL ? min(kend, q0 + BM) : kend;
+  const int ntiles = kend_wg > 0 ? (kend_wg + kBT - 1) / kBT : 0;
+  int kend_w = CAUSAL ? min(kend, qw + 32) : kend;
+  if (qw >= Tq) kend_w = 0;
+  const int ntw = kend_w > 0 ? (kend_w + kBT - 1) / kBT : 0;
+
+  const int64_t qoff = (int64_t)bh * Tq * D, koff = (int64_t)bh * Tk * D;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + koff;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + koff;
+
+  bf16x8 qf[DT], gf[DT];
+  load_row<D>(static_cast<const __bf16*>(p.q) + qoff, row, Tq, g, p.neg != 0, qf);
+  load_row<D>(static_cast<const __bf16*>(p.dout) + qoff, row, Tq, g, false, gf);
+  // D_i = dO_i . O_i (each lane half holds d/2 of the products)
+  float delta;
+  {
+    bf16x8 of[DT];
+    load_row<D>(static_cast<const __bf16*>(p.o) + qoff, row, Tq, g, false, of);
+    float part = 0.f;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += (float)gf[t][e] * (float)of[t][e];
+    delta = pair_sum(part);
+  }
+  float l2 = kPosInf;   // lse in log2 units; +inf makes every weight of an empty row 0
+  if (row < Tq) {
+    const float lse = p.lse[(int64_t)bh * Tq + row];
+    l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
+    if (g == 0) p.delta[(int64_t)bh * Tq + row] = delta;
+  }
+
+  uint32_t src[NLD];
+  tile_src_offsets<D>(w, lane, src);
+  auto load_kv = [&](int j0, char* kt, char* vt) __attribute__((always_inline)) {
+    const uint32_t bytes = (uint32_t)(kend - j0) * ROWB;
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      lds_dma16(kr, kt + (kBwdWaves * u + w) * 1024, src[u]);
+      lds_dma16(vr, vt + (kBwdWaves * u + w) * 1024, src[u]);
+    }
+  };
+  int fr[DT];
+  frag_offsets<D>(c, g, fr);
+  int trd[NO][2];
+  tr_offsets<D>(lane, trd);
+
+  f32x16 acc[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acc[i] = f32x16{};
+  const float cs = p.scale_log2;
+
+  auto step = [&](int it, const char* kt, const char* vt) __attribute__((always_inline)) {
+    const int j0 = it * kBT;
+    const bool edge = (j0 + kBT > kend) || (CAUSAL && j0 + kBT - 1 > qw);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + fr[t]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s, 0, 0, 0);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vt + 32 * hh * ROWB + fr[t]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[t], dp, 0, 0, 0);
+      }
+      // register e: key j0 + 32hh + 16(e/8) + 8g + e%8 of this lane's row
+      f32x16 ds;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cs, -l2));
+        if (edge) {
+          const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+          bool ok = key < kend;
+          if (CAUSAL) ok = ok && key <= row;
+          pe = ok ? pe : 0.f;
+        }
+        ds[e] = pe * (dp[e] - delta);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        f32x8 d8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d8[j] = ds[8 * m + j];
+        const bf16x8 dsb = __builtin_convertvector(d8, bf16x8);
+        const char* kb = kt + (32 * hh + 16 * m) * ROWB;
+#pragma unroll
+        for (int i = 0; i < NO; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(kb + trd[i][0], kb + trd[i][1]), dsb,
+                                                           acc[i], 0, 0, 0);
+      }
+    }
+  };
+
+  if (ntiles > 0) load_kv(0, kb0, vb0);
+  pipeline_barrier<0>();
+  for (int it0 = 0; it0 < ntiles; it0 += 2) {
+    static_for<0, 2>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int it = it0 + u;
+      if (it < ntiles) {
+        if (it + 1 < ntiles) load_kv((it + 1) * kBT, u ? kb0 : kb1, u ? vb0 : vb1);
+        if (it < ntw) step(it, u ? kb1 : kb0, u ? vb1 : vb0);
+        pipeline_barrier<0>();
+      }
+    });
+  }
+  if (row < Tq) store_row<D>(static_cast<__bf16*>(p.dq) + qoff, row, g, p.scale, acc);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV kernel
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool KEYPAD>
+__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  using TG = BwdTile<D>;
+  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT, NO = TG::NO;
+  constexpr int BK = 32 * kBwdWaves;
+  constexpr float kNegInf = -__builtin_inff(), kPosInf = __builtin_inff();
+
+  __shared__ __attribute__((aligned(1024))) char qb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char qb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char gb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char gb1[TILEB];
+  // per tile: lse of its 64 rows in [0, 64), D in [64, 128)
+  __shared__ __attribute__((aligned(256))) float rb0[128];
+  __shared__ __attribute__((aligned(256))) float rb1[128];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  int bh, kt;
+  tile_of_block(p.n_ktiles, false, bh, kt);
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int k0 = kt * BK, kw = k0 + 32 * w, key = kw + c;
+  int kend = Tk;
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  const int nq = (Tq + kBT - 1) / kBT;
+  const int first = CAUSAL ? min(k0 / kBT, nq) : 0;   // rows below k0 see none of these keys
+  const int ntiles = k0 < kend ? nq - first : 0;
+
+  const int64_t qoff = (int64_t)bh * Tq * D, koff = (int64_t)bh * Tk * D;
+  const __bf16* Qg = static_cast<const __bf16*>(p.q) + qoff;
+  const __bf16* Gg = static_cast<const __bf16*>(p.dout) + qoff;
+  const float* Lg = p.lse + (int64_t)bh * Tq;
+  const float* Dg = p.delta + (int64_t)bh * Tq;
+
+  // this lane's key row: K negated for a negative scale (S = scale Q K^T), and V
+  bf16x8 kf[DT], vf[DT];
+  load_row<D>(static_cast<const __bf16*>(p.k) + koff, key, kend, g, p.neg != 0, kf);
+  load_row<D>(static_cast<const __bf16*>(p.v) + koff, key, kend, g, false, vf);
+
+  uint32_t src[NLD];
+  tile_src_offsets<D>(w, lane, src);
+  auto load_tile = [&](int r0, char* qt, char* gt, float* rt) __attribute__((always_inline)) {
+    const uint32_t bytes = (uint32_t)(Tq - r0) * ROWB;
+    const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(Qg + (int64_t)r0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(Gg + (int64_t)r0 * D, bytes);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      lds_dma16(qr, qt + (kBwdWaves * u + w) * 1024, src[u]);
+      lds_dma16(gr, gt + (kBwdWaves * u + w) * 1024, src[u]);
+    }
+    // lse (wave 0) and D (wave 1) of rows r0 .. r0 + 63; rows at or past Tq read as 0
+    if (w < 2) {
+      const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(w == 0 ? Lg + r0 : Dg + r0, (uint32_t)(Tq - r0) * 4);
+      lds_dma4(rr, reinterpret_cast<char*>(rt) + 256 * w, 4 * lane);
+    }
+  };
+  int fr[DT];
+  frag_offsets<D>(c, g, fr);
+  int trd[NO][2];
+  tr_offsets<D>(lane, trd);
+
+  f32x16 adk[NO], adv[NO];
+#pragma unroll
+  for (int i = 0; i < NO; ++i) adk[i] = adv[i] = f32x16{};
+  const float cs = p.scale_log2;
+
+  auto step = [&](int it, const char* qt, const char* gt, const float* rt) __attribute__((always_inline)) {
+    const int r0 = it * kBT;
+    const bool edge = (kw + 32 > kend) || (CAUSAL && r0 < kw + 31) || (r0 + kBT > Tq);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + 32 * hh * ROWB + fr[t]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], s, 0, 0, 0);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt + 32 * hh * ROWB + fr[t]);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
+      }
+      // register e: row r0 + 32hh + 16(e/8) + 8g + e%8 for this lane's key
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int rl = 32 * hh + 16 * m + 8 * g;   // first of the 8 rows (tile-local)
+        const f32x4 la = *reinterpret_cast<const f32x4*>(rt + rl);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(rt + rl + 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(rt + 64 + rl);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(rt + 64 + rl + 4);
+        f32x8 p8, d8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float lse = j < 4 ? la[j] : lb[j - 4];
+          const float dlt = j < 4 ? da[j] : db[j - 4];
+          const float l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + j], cs, -l2));
+          float de = pe * (dp[8 * m + j] - dlt);
+          if (edge) {   // select, not multiply: a masked weight may be inf before it
+            const int rw = r0 + rl + j;
+            bool ok = key < kend && rw < Tq;
+            if (CAUSAL) ok = ok && key <= rw;
+            pe = ok ? pe : 0.f;
+            de = ok ? de : 0.f;
+          }
+          p8[j] = pe;
+          d8[j] = de;
+        }
+        const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
+        const bf16x8 dsb = __builtin_convertvector(d8, bf16x8);
+        const char* gtm = gt + (32 * hh + 16 * m) * ROWB;
+        const char* qtm = qt + (32 * hh + 16 * m) * ROWB;
+#pragma unroll
+        for (int i = 0; i < NO; ++i) {
+          adv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(gtm + trd[i][0], gtm + trd[i][1]), pb,
+                                                           adv[i], 0, 0, 0);
+          adk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qtm + trd[i][0], qtm + trd[i][1]), dsb,
+                                                           adk[i], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  if (ntiles > 0) load_tile(first * kBT, qb0, gb0, rb0);
+  pipeline_barrier<0>();
+  for (int it0 = 0; it0 < ntiles; it0 += 2) {
+    static_for<0, 2>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int it = it0 + u;
+      if (it < ntiles) {
+        if (it + 1 < ntiles) load_tile((first + it + 1) * kBT, u ? qb0 : qb1, u ? gb0 : gb1, u ? rb0 : rb1);
+        step(first + it, u ? qb1 : qb0, u ? gb1 : gb0, u ? rb1 : rb0);
+        pipeline_barrier<0>();
+      }
+    });
+  }
+  if (key < Tk) {
+    store_row<D>(static_cast<__bf16*>(p.dk) + koff, key, g, p.scale, adk);
+    store_row<D>(static_cast<__bf16*>(p.dv) + koff, key, g, 1.0f, adv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <int D, bool C, bool P>
+static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t stream) {
+  BwdParams local = prm;
+  void* args[] = {&local};
+  if (prm.Tq > 0) {
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, C, P>),
+                                         dim3(prm.B * prm.H * prm.n_qtiles), dim3(kBwdThreads), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (prm.Tk > 0)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, C, P>),
+                           dim3(prm.B * prm.H * prm.n_ktiles), dim3(kBwdThreads), args, 0, stream);
+  return hipSuccess;
+}
+
+template <int D>
+static hipError_t launch_bwd_mask(const BwdParams& prm, bool causal, bool keypad, hipStream_t stream) {
+  if (causal) return keypad ? launch_bwd_d<D, true, true>(prm, stream) : launch_bwd_d<D, true, false>(prm, stream);
+  return keypad ? launch_bwd_d<D, false, true>(prm, stream) : launch_bwd_d<D, false, false>(prm, stream);
+}
+
+int bwd_rows_per_block(int) { return 32 * kBwdWaves; }
+int bwd_keys_per_block(int) { return 32 * kBwdWaves; }
+
+hipError_t launch_bwd(const BwdParams& prm, int d, bool causal, bool keypad, hipStream_t stream) {
+  return d == 64 ? launch_bwd_mask<64>(prm, causal, keypad, stream)
+                 : launch_bwd_mask<128>(prm, causal, keypad, stream);
+}
+
+}  // namespace attn

@@ -23,11 +23,38 @@ struct Params {
   int neg;                  // 1 when scale < 0: the kernel negates Q (exact)
   int n_qtiles;             // ceil(Tq / rows_per_block(dt, d))
   int n_wg;                 // B * H * n_qtiles work-groups
+  float* lse;               // optional fp32 [B, H, Tq]: natural-log row normaliser (bf16 path)
+};
+
+// Backward pass arguments (bf16 tensors, fp32 lse and delta).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;         // [B, H, Tq] from the forward
+  float* delta;             // [B, H, Tq] written: D_i = dO_i . O_i
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* key_lens;
+  int B, H, Tq, Tk;
+  float scale_log2;         // |scale| * log2(e) (>= 1e-30)
+  float scale;              // the score scale (dQ = scale dS K, dK = scale dS^T Q)
+  int neg;                  // 1 when scale < 0: the kernels negate Q (exact)
+  int n_qtiles, n_ktiles;   // query / key tiles per (b, head)
 };
 
 // query rows per work-group of the kernel that serves (dt, d)
 int rows_per_block(DType dt, int d);
 hipError_t launch_fwd(const Params& p, DType dt, int d, bool causal, bool keypad, hipStream_t stream);
+
+// backward: query rows per dQ work-group and keys per dK/dV work-group
+int bwd_rows_per_block(int d);
+int bwd_keys_per_block(int d);
+// enqueues the dQ kernel (which also writes delta), then the dK/dV kernel
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool keypad, hipStream_t stream);
 
 }  // namespace attn
 

@@ -1,9 +1,11 @@
 """Tensor-level wrapper over the C ABI (argument marshalling only).
 
 attention() checks the tensors, takes their device pointers and the current
-HIP stream, and calls attn_fwd / attn_fwd_f32.  It never computes attention
-itself: a missing library raises at import, a failed call raises
-AttentionError.
+HIP stream, and calls attn_fwd / attn_fwd_f32; attention_lse() and
+attention_backward() do the same for attn_fwd_lse and attn_bwd, and
+AttentionFunction ties the two into torch.autograd.  Nothing here computes
+attention itself: a missing library raises on first use, a failed call
+raises AttentionError.
 """
 from __future__ import annotations
 
@@ -28,6 +30,47 @@ def default_scale(d_k: int) -> float:
     return float(torch.tensor(1.0 / math.sqrt(d_k), dtype=torch.float32))
 
 
+def _check_qkv(q, k, v, dtypes):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, h, T, d]")
+    B, h, Tq, dk = q.shape
+    Tk = k.shape[2]
+    dv = v.shape[3]
+    if k.shape != (B, h, Tk, dk) or v.shape[:3] != (B, h, Tk):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in dtypes:
+        raise TypeError("q, k, v must share one dtype out of " + ", ".join(str(d) for d in dtypes))
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return B, h, Tq, Tk, dk, dv
+
+
+def _mask_args(B, causal, key_lens):
+    mask = _lib.MASK_CAUSAL if causal else _lib.MASK_NONE
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,):
+            raise ValueError("key_lens must be an int32 [B] device tensor")
+        mask |= _lib.MASK_KEYPAD
+        kl_ptr = key_lens.data_ptr()
+    return mask, kl_ptr
+
+
+def _out_like(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {tuple(shape)} {dtype} tensor")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else (t.data_ptr() or None)
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
               causal: bool = False, key_lens: torch.Tensor | None = None,
               out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
@@ -36,37 +79,84 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     key_lens: optional int32 [B] device tensor (key padding); causal: j <= i.
     The kernel is enqueued on `stream` (default: the current stream).
     """
-    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k, v must be [B, h, T, d]")
-    B, h, Tq, dk = q.shape
-    Tk = k.shape[2]
-    dv = v.shape[3]
-    if k.shape != (B, h, Tk, dk) or v.shape[:3] != (B, h, Tk):
-        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("q, k, v must all be bfloat16 or all float32")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if out is None:
-        out = torch.empty((B, h, Tq, dv), dtype=q.dtype, device=q.device)
-    elif out.shape != (B, h, Tq, dv) or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [B, h, Tq, d_v] tensor of the input dtype")
-    mask = _lib.MASK_CAUSAL if causal else _lib.MASK_NONE
-    kl_ptr = None
-    if key_lens is not None:
-        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,):
-            raise ValueError("key_lens must be an int32 [B] device tensor")
-        mask |= _lib.MASK_KEYPAD
-        kl_ptr = key_lens.data_ptr()
+    B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16, torch.float32))
+    out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
+    mask, kl_ptr = _mask_args(B, causal, key_lens)
     if scale is None:
         scale = default_scale(dk)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
     fn = _lib.attn_fwd if q.dtype == torch.bfloat16 else _lib.attn_fwd_f32
-    status = fn(q.data_ptr() or None, k.data_ptr() or None, v.data_ptr() or None,
-                out.data_ptr() or None, B, h, Tq, Tk, dk, dv, float(scale), mask, kl_ptr, st)
+    status = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h, Tq, Tk, dk, dv, float(scale), mask, kl_ptr, st)
     if status != _lib.OK:
         raise AttentionError(status)
     return out
+
+def attention_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                  causal: bool = False, key_lens: torch.Tensor | None = None,
+                  out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                  stream: torch.cuda.Stream | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """bf16 forward that also returns the fp32 row log-sum-exp [B, h, Tq] (attn_fwd_lse)."""
+    B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16,))
+    out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
+    lse = _out_like(lse, (B, h, Tq), torch.float32, q.device, "lse")
+    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    if scale is None:
+        scale = default_scale(dk)
+    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    status = _lib.attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, h, Tq, Tk, dk, dv,
+                               float(scale), mask, kl_ptr, st)
+    if status != _lib.OK:
+        raise AttentionError(status)
+    return out, lse
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                       dout: torch.Tensor, lse: torch.Tensor, scale: float | None = None,
+                       causal: bool = False, key_lens: torch.Tensor | None = None,
+                       dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+                       dv: torch.Tensor | None = None, delta: torch.Tensor | None = None,
+                       stream: torch.cuda.Stream | None = None):
+    """Gradients (dq, dk, dv) of attention for bf16 tensors (attn_bwd).
+
+    out and lse are what attention_lse returned for these inputs; dout is the
+    gradient of the loss with respect to out.  delta (fp32 [B, h, Tq]) is the
+    kernels' workspace, allocated here when not given.
+    """
+    B, h, Tq, Tk, d_k, d_v = _check_qkv(q, k, v, (torch.bfloat16,))
+    for name, t, shape in (("out", out, (B, h, Tq, d_v)), ("dout", dout, (B, h, Tq, d_v))):
+        if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor of shape {shape}")
+    if tuple(lse.shape) != (B, h, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, h, Tq] tensor")
+    dq = _out_like(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _out_like(dk, k.shape, k.dtype, k.device, "dk")
+    dv = _out_like(dv, v.shape, v.dtype, v.device, "dv")
+    delta = _out_like(delta, (B, h, Tq), torch.float32, q.device, "delta")
+    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    if scale is None:
+        scale = default_scale(d_k)
+    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    status = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta),
+                           _ptr(dq), _ptr(dk), _ptr(dv), B, h, Tq, Tk, d_k, d_v, float(scale), mask, kl_ptr, st)
+    if status != _lib.OK:
+        raise AttentionError(status)
+    return dq, dk, dv
+
+
+class AttentionFunction(torch.autograd.Function):
+    """softmax(scale q k^T) v with gradients: forward attn_fwd_lse, backward attn_bwd (bf16)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale=None, causal=False, key_lens=None):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out, lse = attention_lse(q, k, v, scale=scale, causal=causal, key_lens=key_lens)
+        ctx.save_for_backward(q, k, v, out, lse, key_lens)
+        ctx.scale, ctx.causal = scale, causal
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse, key_lens = ctx.saved_tensors
+        dq, dk, dv = attention_backward(q, k, v, out, dout.contiguous(), lse, scale=ctx.scale,
+                                        causal=ctx.causal, key_lens=key_lens)
+        return dq, dk, dv, None, None, None

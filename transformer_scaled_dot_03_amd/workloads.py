@@ -119,6 +119,15 @@ def make_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu"):
     return q, k, v, key_lens
 
 
+def grad_output(B, h, Tq, dv, dtype="bf16", seed=0):
+    """Upstream gradient dO [B, h, Tq, d_v] for the backward pass: torch.randn
+    from a generator seeded with seed + 1 (so it never repeats the Q/K/V
+    stream of the same seed), rounded once to the dtype."""
+    g = torch.Generator("cpu").manual_seed(seed + 1)
+    x = torch.randn((B, h, Tq, dv), generator=g, dtype=torch.float32)
+    return x.to(TORCH_DTYPES[dtype]).contiguous()
+
+
 def random_inputs(B, h, Tq, Tk, d, dtype="bf16", seed=0, qk_mul=1.0, dv=None):
     """Same recipe for an ad-hoc shape (edge-case tests); d_v defaults to d."""
     dv = d if dv is None else dv
