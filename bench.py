@@ -16,6 +16,10 @@ resident in device memory before the timed region.  Prints ONE JSON line:
   hbm        compulsory bytes (read Q, K, V once, write O once) / time vs 8 TB/s
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host's cores (reported, not a target)
+  backward   (bf16 workloads) the gradient pass on the same inputs: attn_bwd
+             timed with HIP events after one attn_fwd_lse; TFLOP/s counts the
+             algorithmic 10*B*h*Tq*Tk*d flops (halved for causal): recomputed
+             scores, dP, dV, dQ, dK
 """
 from __future__ import annotations
 
@@ -104,6 +108,69 @@ def flops_per_step(w) -> float:
     return f / 2 if w.causal else f
 
 
+def bwd_flops_per_step(w) -> float:
+    """Algorithmic backward flops: five products of B*h*Tq*Tk*d multiply-adds (S recomputed, dP,
+    dV, dQ, dK), 2.5 x the forward's two."""
+    return 2.5 * flops_per_step(w)
+
+
+def bwd_executed_flops(w) -> float:
+    """Matrix-core flops the two backward kernels issue: the dQ kernel computes S, dP, dQ and the
+    dK/dV kernel S, dP, dV, dK (S and dP twice), 3.5 x the forward's."""
+    return 3.5 * flops_per_step(w)
+
+
+def time_backward(torch, tsd, w, qd, kd, vd, kld, steps, warmup):
+    """HIP-event time of one attn_bwd call (both kernels) on the workload."""
+    dev = qd.device
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    mask = (tsd.MASK_CAUSAL if w.causal else 0) | (tsd.MASK_KEYPAD if w.keypad else 0)
+    klp = None if kld is None else kld.data_ptr()
+    from transformer_scaled_dot_03_amd.workloads import grad_output
+    dout = grad_output(w.B, w.h, w.Tq, w.d, seed=0).to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.h, w.Tq), dtype=torch.float32, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    rc = tsd.attn_fwd_lse(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          w.B, w.h, w.Tq, w.Tk, w.d, w.d, w.scale, mask, klp, st)
+    if rc != tsd.OK:
+        raise RuntimeError(f"attn_fwd_lse failed: {tsd.attn_status_str(rc)}")
+    args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            delta.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.h, w.Tq, w.Tk, w.d, w.d,
+            w.scale, mask, klp, st)
+
+    def bstep():
+        rc = tsd.attn_bwd(*args)
+        if rc != tsd.OK:
+            raise RuntimeError(f"attn_bwd failed: {tsd.attn_status_str(rc)}")
+
+    for _ in range(warmup):
+        bstep()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = bwd_flops_per_step(w)
+    return {
+        "what": "attn_bwd (dQ kernel + dK/dV kernel) after one attn_fwd_lse, same inputs, seeded dO",
+        "ms": round(ms, 4),
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "flops_per_step": fl,
+        "frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "executed_tflops": round(bwd_executed_flops(w) / (ms * 1e-3) / 1e12, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "steps": steps,
+    }
+
+
 def compulsory_bytes(w) -> float:
     es = 2 if w.dtype == "bf16" else 4
     return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
@@ -157,6 +224,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the pure-MFMA ceiling measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -250,6 +318,8 @@ def main():
         "hbm": {"compulsory_bytes": cb, "achieved_GBs": round(cb / (ev_ms * 1e-3) / 1e9, 1),
                 "peak_GBs": PEAK_HBM_GBS},
     }
+    if not args.no_backward and w.dtype == "bf16":
+        rec["backward"] = time_backward(torch, tsd, w, qd, kd, vd, kld, args.steps, args.warmup)
     if not args.no_mfma_probe and w.dtype == "bf16":
         rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:
