@@ -16,6 +16,10 @@ resident in device memory before the timed region.  Prints ONE JSON line:
   hbm        compulsory bytes (read Q, K, V once, write O once) / time vs 8 TB/s
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
              workload on this host's cores (reported, not a target)
+  decode     single-row decode (attn_decode) on its own workload (default B8 h16,
+             one query row per head against a 16384-entry K/V cache, d128):
+             compulsory bytes (the valid K/V rows, q, out) / HIP-event time vs
+             8 TB/s -- the decode step is bound by HBM
   backward   (bf16 workloads) the gradient pass on the same inputs: attn_bwd
              timed with HIP events after one attn_fwd_lse; TFLOP/s counts the
              algorithmic 10*B*h*Tq*Tk*d flops (halved for causal): recomputed
@@ -171,6 +175,60 @@ def time_backward(torch, tsd, w, qd, kd, vd, kld, steps, warmup):
     }
 
 
+def decode_bytes(w, key_lens) -> float:
+    """Compulsory bytes of one decode step: each (b, head) reads its L_b valid K and V rows and
+    its query row and writes one output row (bf16)."""
+    rows = w.B * w.Tk if key_lens is None else int(key_lens.clamp(0, w.Tk).sum())
+    return float(2 * w.h * (2 * rows * w.d + 2 * w.B * w.d))
+
+
+def time_decode(torch, tsd, name, steps, warmup):
+    """HIP-event time of attn_decode (split + merge kernels) on a decode workload."""
+    from transformer_scaled_dot_03_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, kl = make_inputs(w, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    kld = None if kl is None else kl.to(dev)
+    del q, k, v
+    out = torch.empty_like(qd)
+    nbytes = tsd.attn_decode_workspace_bytes(w.B, w.h, w.Tk, w.d)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    mask = tsd.MASK_KEYPAD if w.keypad else 0
+    args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), w.B, w.h, w.Tk, w.d, w.d, w.scale, mask,
+            None if kld is None else kld.data_ptr(), ws.data_ptr(), nbytes, stream.cuda_stream)
+
+    def dstep():
+        rc = tsd.attn_decode(*args)
+        if rc != tsd.OK:
+            raise RuntimeError(f"attn_decode failed: {tsd.attn_status_str(rc)}")
+
+    for _ in range(warmup):
+        dstep()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        dstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nb = decode_bytes(w, kl)
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {
+        "workload": name,
+        "what": "attn_decode (split + merge kernels), one query row per (b, head), seeded inputs",
+        "ms": round(ms, 4),
+        "compulsory_bytes": nb,
+        "achieved_GBs": round(gbs, 1),
+        "peak_GBs": PEAK_HBM_GBS,
+        "frac": round(gbs / PEAK_HBM_GBS, 4),
+        "steps": steps,
+    }
+
+
 def compulsory_bytes(w) -> float:
     es = 2 if w.dtype == "bf16" else 4
     return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
@@ -225,6 +283,8 @@ def main():
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the pure-MFMA ceiling measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--decode-workload", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -320,6 +380,9 @@ def main():
     }
     if not args.no_backward and w.dtype == "bf16":
         rec["backward"] = time_backward(torch, tsd, w, qd, kd, vd, kld, args.steps, args.warmup)
+    if not args.no_decode:
+        from transformer_scaled_dot_03_amd.workloads import DECODE_HEADLINE
+        rec["decode"] = time_decode(torch, tsd, args.decode_workload or DECODE_HEADLINE, args.steps, args.warmup)
     if not args.no_mfma_probe and w.dtype == "bf16":
         rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:

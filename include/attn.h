@@ -1,6 +1,6 @@
 /*
- * attn.h -- C ABI of libattn.so: fused scaled dot-product attention forward
- * for AMD Instinct MI355X (gfx950).
+ * attn.h -- C ABI of libattn.so: fused scaled dot-product attention (forward,
+ * log-sum-exp, backward, single-row decode) for AMD Instinct MI355X (gfx950).
  *
  * Operation (per batch entry b and head, for every query row i):
  *
@@ -49,6 +49,7 @@
 #ifndef ATTN_H_
 #define ATTN_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -76,6 +77,7 @@ enum {
   ATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
   ATTN_ERR_TOO_LARGE = -8,   /* more than 2^31-1 work-groups, or one head's rows of a tensor
                                 exceed 4 GiB (T * d * element size >= 2^32) */
+  ATTN_ERR_WORKSPACE = -9,   /* attn_decode: workspace NULL or smaller than attn_decode_workspace_bytes() */
   ATTN_ERR_HIP = -100        /* the kernel launch failed; see attn_last_hip_error() */
 };
 
@@ -158,6 +160,40 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              const float* lse, float* delta, void* dq, void* dk, void* dv,
              int B, int h, int Tq, int Tk, int d_k, int d_v, float scale,
              int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
+ * attn_decode: the operation above for one query row per (b, head) -- the
+ * generation loop of the pages, where the decoder emits one token at a time
+ * and the newest position attends every cached key (muhitai.com, "What Is
+ * Masked Attention?"; notebook chapter, "Masked Attention in the Decoder":
+ * the newest row of the causal mask allows all earlier keys).  bfloat16 q, k,
+ * v and out; fp32 scores, weights and sums (no bfloat16 rounding before the
+ * weighted sum); the output is rounded once to bfloat16.
+ *   q, out      : [B, h, 1, d] (i.e. [B, h, d]) bfloat16
+ *   k, v        : [B, h, Tk, d] bfloat16, the key/value cache
+ *   mask_kind   : ATTN_MASK_NONE or ATTN_MASK_KEYPAD (per-sequence cache
+ *                 lengths key_lens[b], clamped to [0, Tk]); ATTN_MASK_CAUSAL is
+ *                 rejected (ATTN_ERR_MASK): under the top-left causal reading
+ *                 of attn_fwd a single row 0 would see key 0 only, while the
+ *                 newest decode position sees the whole valid cache
+ *   workspace   : caller-owned device memory of at least
+ *                 attn_decode_workspace_bytes(B, h, Tk, d) bytes, 16-byte
+ *                 aligned, not overlapping any tensor; it holds the per-split
+ *                 partial results between the two kernels and needs no
+ *                 initialisation.  Calls that share a workspace must not
+ *                 overlap in time (same stream, or synchronised).
+ *   other arguments as for attn_fwd; d_k = d_v in {64, 128}.
+ * Two kernels are enqueued on `stream`: a split kernel (one work-group per
+ * (b, head, chunk of keys)) and a merge kernel.  A row with no valid key
+ * (L_b = 0 or Tk = 0) gets zeros.  B or h = 0 is a no-op.
+ */
+int attn_decode(const void* q, const void* k, const void* v, void* out,
+                int B, int h, int Tk, int d_k, int d_v, float scale,
+                int mask_kind, const int32_t* key_lens,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attn_decode needs for (B, h, Tk, d); 0 for invalid sizes. */
+size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_str(int status);

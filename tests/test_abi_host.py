@@ -39,8 +39,8 @@ def _declared_enum():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_bwd", "attn_status_str", "attn_last_hip_error",
-         "attn_version"])
+        ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_bwd", "attn_decode", "attn_decode_workspace_bytes",
+         "attn_status_str", "attn_last_hip_error", "attn_version"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(L):
 def test_status_constants_match_header(L):
     enum = _declared_enum()
     assert enum["ATTN_OK"] == L.OK
-    for name in ("NULL", "SHAPE", "HEADDIM", "MASK", "ALIAS", "ALIGN", "SCALE", "TOO_LARGE", "HIP"):
+    for name in ("NULL", "SHAPE", "HEADDIM", "MASK", "ALIAS", "ALIGN", "SCALE", "TOO_LARGE", "WORKSPACE", "HIP"):
         assert enum["ATTN_ERR_" + name] == getattr(L, "ERR_" + name)
     for name in ("NONE", "CAUSAL", "KEYPAD"):
         assert enum["ATTN_MASK_" + name] == getattr(L, "MASK_" + name)
@@ -62,7 +62,7 @@ def test_status_constants_match_header(L):
 
 def test_status_strings_and_version(L):
     for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_HEADDIM, L.ERR_MASK, L.ERR_ALIAS,
-                 L.ERR_ALIGN, L.ERR_SCALE, L.ERR_TOO_LARGE, L.ERR_HIP):
+                 L.ERR_ALIGN, L.ERR_SCALE, L.ERR_TOO_LARGE, L.ERR_WORKSPACE, L.ERR_HIP):
         s = L.attn_status_str(code)
         assert s and s != "unknown status"
     assert L.attn_status_str(12345) == "unknown status"
@@ -220,6 +220,60 @@ def test_bwd_bad_arguments_rejected_before_any_launch(L, over, code):
                                                                  "dq", "dk", "dv")})])
 def test_bwd_empty_problem_is_a_no_op(L, over):
     assert _call_bwd(L, **over) == L.OK
+
+
+# decode: fake addresses, never dereferenced
+DEC = dict(q=0x10000000, k=0x20000000, v=0x30000000, out=0x40000000, B=4, h=8, Tk=5000, d_k=128, d_v=128,
+           scale=0.088, mask_kind=0, key_lens=None, ws=0x50000000, ws_bytes=1 << 26, stream=None)
+
+
+def _call_dec(L, **over):
+    a = dict(DEC)
+    a.update(over)
+    return L.attn_decode(a["q"], a["k"], a["v"], a["out"], a["B"], a["h"], a["Tk"], a["d_k"], a["d_v"],
+                         a["scale"], a["mask_kind"], a["key_lens"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_decode_workspace_size(L):
+    assert L.attn_decode_workspace_bytes(0, 8, 100, 64) == 0
+    assert L.attn_decode_workspace_bytes(2, 8, 100, 96) == 0
+    assert L.attn_decode_workspace_bytes(2, 8, -1, 64) == 0
+    small = L.attn_decode_workspace_bytes(1, 1, 10, 64)
+    assert small > 0 and small % 256 == 0
+    # grows with the cache length (more splits) and with d
+    assert L.attn_decode_workspace_bytes(1, 1, 100000, 64) > small
+    assert L.attn_decode_workspace_bytes(1, 1, 10, 128) > small
+    # at least one partial (max, sum, d outputs) per (b, head)
+    assert L.attn_decode_workspace_bytes(3, 5, 0, 64) >= 3 * 5 * (64 + 2) * 4
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "ERR_SHAPE"),
+    (dict(d_v=64), "ERR_SHAPE"),
+    (dict(d_k=80, d_v=80), "ERR_HEADDIM"),
+    (dict(mask_kind=1), "ERR_MASK"),            # causal is not a decode mask
+    (dict(mask_kind=3), "ERR_MASK"),
+    (dict(mask_kind=2), "ERR_MASK"),            # key padding without key_lens
+    (dict(scale=float("nan")), "ERR_SCALE"),
+    (dict(q=None), "ERR_NULL"),
+    (dict(k=None), "ERR_NULL"),
+    (dict(out=None), "ERR_NULL"),
+    (dict(ws=None), "ERR_WORKSPACE"),
+    (dict(ws_bytes=1024), "ERR_WORKSPACE"),
+    (dict(ws=0x50000008), "ERR_ALIGN"),
+    (dict(out=0x40000004), "ERR_ALIGN"),
+    (dict(ws=0x20000000 + 4096), "ERR_ALIAS"),  # workspace inside k
+    (dict(out=0x10000000), "ERR_ALIAS"),
+    (dict(Tk=1 << 25), "ERR_TOO_LARGE"),
+])
+def test_decode_bad_arguments_rejected_before_any_launch(L, over, code):
+    assert _call_dec(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+def test_decode_empty_is_a_no_op(L):
+    assert _call_dec(L, B=0, q=None, out=None, ws=None) == L.OK
+    assert _call_dec(L, h=0) == L.OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -26,6 +26,7 @@ ERR_ALIAS = -5
 ERR_ALIGN = -6
 ERR_SCALE = -7
 ERR_TOO_LARGE = -8
+ERR_WORKSPACE = -9
 ERR_HIP = -100
 
 # names and C signatures of every exported entry point (kept in step with attn.h)
@@ -39,6 +40,8 @@ SIGNATURES = {
     "attn_fwd_f32": (_I, _FWD_ARGS),
     "attn_fwd_lse": (_I, _FWD_LSE_ARGS),
     "attn_bwd": (_I, _BWD_ARGS),
+    "attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]),
+    "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
     "attn_version": (ctypes.c_char_p, []),
@@ -95,6 +98,18 @@ def attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v,
     """bf16 attention backward: dq, dk, dv (and delta) from out, dout and lse (attn.h `attn_bwd`)."""
     return raw_library().attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v, scale,
                                   mask_kind, key_lens, stream)
+
+
+def attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace, workspace_bytes,
+                stream) -> int:
+    """bf16 single-row decode attention over a K/V cache (attn.h `attn_decode`)."""
+    return raw_library().attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace,
+                                     workspace_bytes, stream)
+
+
+def attn_decode_workspace_bytes(B, h, Tk, d) -> int:
+    """Workspace bytes attn_decode needs (attn.h `attn_decode_workspace_bytes`)."""
+    return raw_library().attn_decode_workspace_bytes(B, h, Tk, d)
 
 
 def attn_status_str(status: int) -> str:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_api.hip"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_api.hip"]
 # measurement aid for the benchmark: pure matrix-core loop (include/mfma_probe.h)
 PROBE_LIB_PATH = os.path.join(PKG, "libmfma_probe.so")
 PROBE_SOURCES = ["mfma_probe.hip"]

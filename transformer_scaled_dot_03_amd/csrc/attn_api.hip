@@ -170,9 +170,91 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   return ATTN_OK;
 }
 
+// workspace layout of attn_decode: partial outputs, then partial (max, sum)
+struct DecodeWorkspace {
+  int n_split, keys_per_split;
+  size_t acc_bytes, bytes;
+};
+
+DecodeWorkspace decode_workspace(int B, int h, int Tk, int d) {
+  DecodeWorkspace w;
+  w.keys_per_split = attn::decode_keys_per_split(B, h, Tk);
+  w.n_split = attn::decode_splits(B, h, Tk);
+  const size_t parts = static_cast<size_t>(B) * h * w.n_split;
+  w.acc_bytes = (parts * d * 4 + 255) & ~static_cast<size_t>(255);
+  w.bytes = w.acc_bytes + ((parts * 2 * 4 + 255) & ~static_cast<size_t>(255));
+  return w;
+}
+
+int decode(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k, int d_v,
+           float scale, int mask_kind, const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+           hipStream_t stream) {
+  if (B < 0 || h < 0 || Tk < 0 || d_k < 0 || d_v < 0) return ATTN_ERR_SHAPE;
+  if (d_k != d_v) return ATTN_ERR_SHAPE;
+  if (d_k != 64 && d_k != 128) return ATTN_ERR_HEADDIM;
+  if (mask_kind & ~ATTN_MASK_KEYPAD) return ATTN_ERR_MASK;  // causal is not a decode mask
+  const bool keypad = (mask_kind & ATTN_MASK_KEYPAD) != 0;
+  if (keypad && key_lens == nullptr) return ATTN_ERR_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || h == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  if (Tk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
+  if (misaligned(q, 16) || misaligned(out, 16) || misaligned(workspace, 16) ||
+      (Tk > 0 && (misaligned(k, 16) || misaligned(v, 16))))
+    return ATTN_ERR_ALIGN;
+  if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
+  const int64_t bh = static_cast<int64_t>(B) * h;
+  if (static_cast<int64_t>(Tk) * d_k * 2 > 0xffffffffLL) return ATTN_ERR_TOO_LARGE;
+  const DecodeWorkspace ws = decode_workspace(B, h, Tk, d_k);
+  if (bh * ws.n_split > 0x7fffffffLL || bh > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  if (workspace_bytes < ws.bytes) return ATTN_ERR_WORKSPACE;
+
+  typedef unsigned __int128 u128;
+  const u128 nq = (u128)bh * d_k * 2, nkv = (u128)bh * Tk * d_k * 2, nw = ws.bytes;
+  if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nkv) || overlaps(out, nq, v, nkv) ||
+      overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) || overlaps(workspace, nw, v, nkv) ||
+      overlaps(workspace, nw, out, nq))
+    return ATTN_ERR_ALIAS;
+
+  attn::DecParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = out;
+  p.key_lens = keypad ? key_lens : nullptr;
+  p.part_acc = static_cast<float*>(workspace);
+  p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_bytes);
+  p.B = B;
+  p.H = h;
+  p.Tk = Tk;
+  p.keys_per_split = ws.keys_per_split;
+  p.n_split = ws.n_split;
+  p.scale_log2 = scale_log2(scale);
+  p.neg = scale < 0.f ? 1 : 0;
+  const hipError_t e = attn::launch_decode(p, d_k, keypad, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d) {
+  if (B <= 0 || h <= 0 || Tk < 0 || (d != 64 && d != 128)) return 0;
+  return decode_workspace(B, h, Tk, d).bytes;
+}
+
+int attn_decode(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k, int d_v,
+                float scale, int mask_kind, const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  return decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace, workspace_bytes,
+                stream);
+}
 
 int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int h, int Tq, int Tk,
              int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
@@ -212,6 +294,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_bytes()";
     case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";

@@ -50,6 +50,29 @@ struct BwdParams {
 int rows_per_block(DType dt, int d);
 hipError_t launch_fwd(const Params& p, DType dt, int d, bool causal, bool keypad, hipStream_t stream);
 
+// Decode (one query row per (b, head)) split over the keys: arguments of the
+// split kernel and of the merge kernel.
+struct DecParams {
+  const void* q;            // bf16 [B*H, d]
+  const void* k;            // bf16 [B*H, Tk, d]
+  const void* v;
+  void* o;                  // bf16 [B*H, d]
+  const int32_t* key_lens;  // device [B] or nullptr
+  float* part_acc;          // fp32 [B*H, n_split, d]: unnormalised partial outputs
+  float* part_ml;           // fp32 [B*H, n_split, 2]: partial (max, sum), log2 units
+  int B, H, Tk;
+  int keys_per_split;       // multiple of 256
+  int n_split;
+  float scale_log2;         // |scale| * log2(e) (>= 1e-30)
+  int neg;                  // 1 when scale < 0: q is negated (exact)
+};
+
+// keys per split work-group and split count for a decode problem (the same
+// function sizes the workspace and the launch)
+int decode_keys_per_split(int B, int H, int Tk);
+int decode_splits(int B, int H, int Tk);
+hipError_t launch_decode(const DecParams& p, int d, bool keypad, hipStream_t stream);
+
 // backward: query rows per dQ work-group and keys per dK/dV work-group
 int bwd_rows_per_block(int d);
 int bwd_keys_per_block(int d);

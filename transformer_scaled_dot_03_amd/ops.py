@@ -160,3 +160,34 @@ class AttentionFunction(torch.autograd.Function):
         dq, dk, dv = attention_backward(q, k, v, out, dout.contiguous(), lse, scale=ctx.scale,
                                         causal=ctx.causal, key_lens=key_lens)
         return dq, dk, dv, None, None, None
+
+
+def decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                     key_lens: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None,
+                     stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """One query row per (b, head) against a bf16 K/V cache (attn_decode).
+
+    q: [B, h, 1, d]; k, v: [B, h, Tk, d]; key_lens: optional int32 [B] device
+    tensor of valid cache lengths.  workspace: optional uint8 device tensor of
+    at least attn_decode_workspace_bytes(B, h, Tk, d) bytes (allocated here
+    when not given; calls sharing one must not overlap in time).
+    """
+    B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16,))
+    if Tq != 1:
+        raise ValueError("decode_attention takes one query row per (b, head): q must be [B, h, 1, d]")
+    out = _out_like(out, (B, h, 1, dv), q.dtype, q.device, "out")
+    mask, kl_ptr = _mask_args(B, False, key_lens)
+    need = _lib.attn_decode_workspace_bytes(B, h, Tk, dk) if B > 0 and h > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    if scale is None:
+        scale = default_scale(dk)
+    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    status = _lib.attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h, Tk, dk, dv, float(scale), mask, kl_ptr,
+                              _ptr(workspace), workspace.numel(), st)
+    if status != _lib.OK:
+        raise AttentionError(status)
+    return out

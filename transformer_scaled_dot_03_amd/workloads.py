@@ -85,10 +85,19 @@ WORKLOADS = {
     "long_causal_bf16_b1h16t16384d128": Workload(
         "long_causal_bf16_b1h16t16384d128", 1, 16, 16384, 16384, 128, "bf16", MASK_CAUSAL,
         SCALE_D128, desc="long-sequence attention, causal"),
+    # one query row per (b, head) against a key/value cache: the decoder's generation step
+    "decode_bf16_b8h16k16384d128": Workload(
+        "decode_bf16_b8h16k16384d128", 8, 16, 1, 16384, 128, "bf16", MASK_NONE, SCALE_D128,
+        desc="decode step: one new row per head against a 16384-entry cache (K+V 1 GiB)"),
+    "decode_keypad_bf16_b64h8k4096d64": Workload(
+        "decode_keypad_bf16_b64h8k4096d64", 64, 8, 1, 4096, 64, "bf16", MASK_KEYPAD, SCALE_D64,
+        key_len_range=(256, 4096), desc="decode step, ragged caches L~U[256,4096] (K+V 512 MiB)"),
 }
 
 # the workload the throughput figure is quoted on (non-causal, T >= 1024)
 HEADLINE = "long_bf16_b1h16t16384d128"
+# the workload the decode measurement is quoted on
+DECODE_HEADLINE = "decode_bf16_b8h16k16384d128"
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
