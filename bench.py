@@ -46,16 +46,21 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-KERNEL_SOURCES = ["attn_fwd_kernel.hip", "attn_launch.h", "attn_api.hip"]
+# what the forward kernel is compiled from: its source, the device helpers it
+# includes and its argument struct (the rest of attn_launch.h declares other kernels)
+KERNEL_SOURCES = ["attn_fwd_kernel.hip", "attn_device.h"]
 
 
 def kernel_source_digest() -> str:
-    """Short hash of the attention kernel sources (keys the committed counter data)."""
+    """Short hash of the forward kernel's sources (keys the committed counter data)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "csrc")
     for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    launch = open(os.path.join(csrc, "attn_launch.h"), "rb").read()
+    m = re.search(rb"struct Params \{.*?\};", launch, flags=re.S)
+    h.update(b"Params\0" + (m.group(0) if m else launch))
     return h.hexdigest()[:16]
 
 
