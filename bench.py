@@ -20,6 +20,9 @@ resident in device memory before the timed region.  Prints ONE JSON line:
              one query row per head against a 16384-entry K/V cache, d128):
              compulsory bytes (the valid K/V rows, q, out) / HIP-event time vs
              8 TB/s -- the decode step is bound by HBM
+  weights    attn_fwd_weights on the decoder-causal workload (B16 h16 T1024
+             d64): the fp32 weight matrix written per second; the weights
+             kernel's time is the call's minus attn_fwd_lse's (both HIP events)
   backward   (bf16 workloads) the gradient pass on the same inputs: attn_bwd
              timed with HIP events after one attn_fwd_lse; TFLOP/s counts the
              algorithmic 10*B*h*Tq*Tk*d flops (halved for causal): recomputed
@@ -234,6 +237,65 @@ def time_decode(torch, tsd, name, steps, warmup):
     }
 
 
+def time_weights(torch, tsd, name, steps, warmup):
+    """HIP-event times of attn_fwd_weights and attn_fwd_lse on one workload; the difference is the
+    weights kernel, which writes B*h*Tq*Tk fp32 values."""
+    from transformer_scaled_dot_03_amd.workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v, kl = make_inputs(w, seed=0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    kld = None if kl is None else kl.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.h, w.Tq), dtype=torch.float32, device=dev)
+    wts = torch.empty((w.B, w.h, w.Tq, w.Tk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    mask = (tsd.MASK_CAUSAL if w.causal else 0) | (tsd.MASK_KEYPAD if w.keypad else 0)
+    klp = None if kld is None else kld.data_ptr()
+    head = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr())
+    tail = (w.B, w.h, w.Tq, w.Tk, w.d, w.d, w.scale, mask, klp, stream.cuda_stream)
+
+    def run(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def call_w():
+        if tsd.attn_fwd_weights(*head, wts.data_ptr(), *tail) != tsd.OK:
+            raise RuntimeError("attn_fwd_weights failed")
+
+    def call_f():
+        if tsd.attn_fwd_lse(*head, *tail) != tsd.OK:
+            raise RuntimeError("attn_fwd_lse failed")
+
+    ms_w = run(call_w)
+    ms_f = run(call_f)
+    ms_fill = run(lambda: wts.fill_(0.5))     # a plain write of the same bytes: the write ceiling here
+    nbytes = float(w.B * w.h * w.Tq * w.Tk * 4)
+    ms_k = max(ms_w - ms_f, 1e-6)
+    return {
+        "workload": name,
+        "what": "attn_fwd_weights (forward + weights kernel); weights kernel = call minus attn_fwd_lse",
+        "ms_call": round(ms_w, 4),
+        "ms_forward": round(ms_f, 4),
+        "ms_weights_kernel": round(ms_k, 4),
+        "weights_bytes": nbytes,
+        "achieved_GBs": round(nbytes / (ms_k * 1e-3) / 1e9, 1),
+        "peak_GBs": PEAK_HBM_GBS,
+        "frac": round(nbytes / (ms_k * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "fill_GBs": round(nbytes / (ms_fill * 1e-3) / 1e9, 1),
+        "steps": steps,
+    }
+
+
 def compulsory_bytes(w) -> float:
     es = 2 if w.dtype == "bf16" else 4
     return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
@@ -289,6 +351,7 @@ def main():
                     help="skip the pure-MFMA ceiling measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-weights", action="store_true", help="skip the weights-output measurement")
     ap.add_argument("--decode-workload", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -388,6 +451,8 @@ def main():
     if not args.no_decode:
         from transformer_scaled_dot_03_amd.workloads import DECODE_HEADLINE
         rec["decode"] = time_decode(torch, tsd, args.decode_workload or DECODE_HEADLINE, args.steps, args.warmup)
+    if not args.no_weights:
+        rec["weights"] = time_weights(torch, tsd, "dec_causal_bf16_b16h16t1024d64", args.steps, args.warmup)
     if not args.no_mfma_probe and w.dtype == "bf16":
         rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:

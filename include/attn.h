@@ -162,6 +162,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              int mask_kind, const int32_t* key_lens, hipStream_t stream);
 
 /*
+ * attn_fwd_weights: attn_fwd_lse, then the attention weights themselves,
+ *
+ *     weights[b,h,i,j] = w_ij = exp(s_ij - lse[b,h,i])   (0 where j is not allowed),
+ *
+ * written in full as fp32 [B, h, Tq, Tk] -- the second result of the pages'
+ * attention() (aiany.app explainer, Step 6: the matrix A = softmax(S) whose
+ * rows sum to 1; the cuijiawei.cn snippet returns output and weights), for
+ * inspection such as attention heat maps.  The scores are recomputed from q
+ * and k; the normaliser is the forward's own, so each row of weights sums to
+ * 1 within the bfloat16 rounding of the forward's probabilities (2^-9).
+ *   lse     : fp32 [B, h, Tq] (required; as attn_fwd_lse)
+ *   weights : fp32 [B, h, Tq, Tk], 16-byte aligned, overlapping no other tensor
+ *   other arguments as for attn_fwd (bfloat16 q, k, v, out).
+ * Two kernels are enqueued on `stream` (the forward, then the weights).  Rows
+ * with no allowed key get all-zero weights.  B, h or Tq = 0 is a no-op;
+ * Tk = 0 writes zero outputs and -inf lse (weights unused).
+ */
+int attn_fwd_weights(const void* q, const void* k, const void* v, void* out, float* lse,
+                     float* weights, int B, int h, int Tq, int Tk, int d_k, int d_v,
+                     float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
  * attn_decode: the operation above for one query row per (b, head) -- the
  * generation loop of the pages, where the decoder emits one token at a time
  * and the newest position attends every cached key (muhitai.com, "What Is

@@ -39,7 +39,8 @@ def _declared_enum():
 
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
-        ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_bwd", "attn_decode", "attn_decode_workspace_bytes",
+        ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_weights", "attn_bwd", "attn_decode",
+         "attn_decode_workspace_bytes",
          "attn_status_str", "attn_last_hip_error", "attn_version"])
 
 
@@ -159,6 +160,38 @@ def test_fwd_lse_bad_arguments(L, over, code):
 def test_fwd_lse_empty_is_a_no_op(L):
     assert _call_lse(L, Tq=0, lse=None) == L.OK
     assert _call_lse(L, B=0, lse=None, q=None, out=None) == L.OK
+
+
+WTS = 0x70000000
+
+
+def _call_wts(L, **over):
+    a = dict(GOOD, lse=LSE, weights=WTS)
+    a.update(over)
+    return L.attn_fwd_weights(a["q"], a["k"], a["v"], a["out"], a["lse"], a["weights"], a["B"], a["h"], a["Tq"],
+                              a["Tk"], a["d_k"], a["d_v"], a["scale"], a["mask_kind"], a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(weights=None), "ERR_NULL"),
+    (dict(lse=None), "ERR_NULL"),
+    (dict(weights=WTS + 8), "ERR_ALIGN"),
+    (dict(weights=Q + 1024), "ERR_ALIAS"),
+    (dict(weights=LSE - 64), "ERR_ALIAS"),       # its first bytes run into lse
+    (dict(weights=O), "ERR_ALIAS"),
+    (dict(d_k=32, d_v=32, weights=None), "ERR_HEADDIM"),   # the forward's checks come first
+    (dict(mask_kind=5), "ERR_MASK"),
+    (dict(scale=float("inf")), "ERR_SCALE"),
+    (dict(Tq=-1), "ERR_SHAPE"),
+])
+def test_fwd_weights_bad_arguments(L, over, code):
+    assert _call_wts(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+def test_fwd_weights_empty_is_a_no_op(L):
+    assert _call_wts(L, Tq=0, lse=None, weights=None) == L.OK
+    assert _call_wts(L, B=0, q=None, out=None, lse=None, weights=None) == L.OK
 
 
 # backward: fake addresses 256 MiB apart, never dereferenced

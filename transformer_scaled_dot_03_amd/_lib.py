@@ -40,6 +40,7 @@ SIGNATURES = {
     "attn_fwd_f32": (_I, _FWD_ARGS),
     "attn_fwd_lse": (_I, _FWD_LSE_ARGS),
     "attn_bwd": (_I, _BWD_ARGS),
+    "attn_fwd_weights": (_I, [_P] * 6 + [_I] * 6 + [ctypes.c_float, _I, _P, _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
@@ -98,6 +99,13 @@ def attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v,
     """bf16 attention backward: dq, dk, dv (and delta) from out, dout and lse (attn.h `attn_bwd`)."""
     return raw_library().attn_bwd(q, k, v, out, dout, lse, delta, dq, dk, dv, B, h, Tq, Tk, d_k, d_v, scale,
                                   mask_kind, key_lens, stream)
+
+
+def attn_fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+                     stream) -> int:
+    """bf16 forward plus fp32 log-sum-exp and fp32 attention weights (attn.h `attn_fwd_weights`)."""
+    return raw_library().attn_fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, mask_kind,
+                                          key_lens, stream)
 
 
 def attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace, workspace_bytes,

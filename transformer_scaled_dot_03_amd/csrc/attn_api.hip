@@ -170,6 +170,58 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   return ATTN_OK;
 }
 
+int fwd_weights(const void* q, const void* k, const void* v, void* out, float* lse, float* weights, int B, int h,
+                int Tq, int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
+                hipStream_t stream) {
+  // the argument checks of the forward, in its order, before the weights' own
+  if (B < 0 || h < 0 || Tq < 0 || Tk < 0 || d_k < 0 || d_v < 0 || d_k != d_v) return ATTN_ERR_SHAPE;
+  if (d_k != 64 && d_k != 128) return ATTN_ERR_HEADDIM;
+  if ((mask_kind & ~(ATTN_MASK_CAUSAL | ATTN_MASK_KEYPAD)) ||
+      ((mask_kind & ATTN_MASK_KEYPAD) && key_lens == nullptr))
+    return ATTN_ERR_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || h == 0 || Tq == 0) return ATTN_OK;
+  if (lse == nullptr || (Tk > 0 && weights == nullptr)) return ATTN_ERR_NULL;
+  if (weights != nullptr && misaligned(weights, 16)) return ATTN_ERR_ALIGN;
+  {
+    const int64_t bm = attn::weights_rows_per_block(d_k);
+    if (static_cast<int64_t>(B) * h * ((Tq + bm - 1) / bm) > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  }
+  if (Tk > 0) {
+    typedef unsigned __int128 u128;
+    const u128 bh = (u128)B * h;
+    const u128 nw = bh * Tq * Tk * 4, nq = bh * Tq * d_k * 2, nkv = bh * Tk * d_k * 2, no = bh * Tq * d_v * 2;
+    const u128 nl = bh * Tq * 4;
+    if (overlaps(weights, nw, q, nq) || overlaps(weights, nw, k, nkv) || overlaps(weights, nw, v, nkv) ||
+        overlaps(weights, nw, out, no) || overlaps(weights, nw, lse, nl))
+      return ATTN_ERR_ALIAS;
+  }
+  const int st = fwd(attn::DType::BF16, q, k, v, out, lse, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
+                     stream);
+  if (st != ATTN_OK || B == 0 || h == 0 || Tq == 0 || Tk == 0) return st;
+  const int64_t bm = attn::weights_rows_per_block(d_k);
+  attn::WtsParams p;
+  p.q = q;
+  p.k = k;
+  p.lse = lse;
+  p.w = weights;
+  p.key_lens = (mask_kind & ATTN_MASK_KEYPAD) ? key_lens : nullptr;
+  p.B = B;
+  p.H = h;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.scale_log2 = scale_log2(scale);
+  p.neg = scale < 0.f ? 1 : 0;
+  p.n_qtiles = static_cast<int>((Tq + bm - 1) / bm);
+  const hipError_t e = attn::launch_weights(p, d_k, (mask_kind & ATTN_MASK_CAUSAL) != 0,
+                                            (mask_kind & ATTN_MASK_KEYPAD) != 0, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 // workspace layout of attn_decode: partial outputs, then partial (max, sum)
 struct DecodeWorkspace {
   int n_split, keys_per_split;
@@ -243,6 +295,12 @@ int decode(const void* q, const void* k, const void* v, void* out, int B, int h,
 }  // namespace
 
 extern "C" {
+
+int attn_fwd_weights(const void* q, const void* k, const void* v, void* out, float* lse, float* weights, int B,
+                     int h, int Tq, int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
+                     hipStream_t stream) {
+  return fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream);
+}
 
 size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d) {
   if (B <= 0 || h <= 0 || Tk < 0 || (d != 64 && d != 128)) return 0;

@@ -404,6 +404,127 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
 }
 
 // ---------------------------------------------------------------------------
+// Attention weights output: w_ij = exp(scale s_ij - lse_i), masked entries 0,
+// the whole [Tq, Tk] matrix of every (b, head) written as fp32.  One
+// work-group per 128 query rows walks all key tiles of 64: tiles inside the
+// causal / padding limit recompute S^T = K Q^T on the matrix cores (K tiles
+// double-buffered in LDS as in the dQ kernel), tiles past it are written as
+// zeros without loading anything.  Lane (c, g) stores 8 consecutive keys of
+// its row per 16-key slice (two 16-byte stores; the two lanes of a row write
+// 64 contiguous bytes), scalar stores when Tk is not a multiple of 4 or at the
+// ragged end.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool KEYPAD>
+__global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams p) {
+  using TG = BwdTile<D>;
+  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT;
+  constexpr int BM = 32 * kBwdWaves;
+  constexpr float kNegInf = -__builtin_inff(), kPosInf = __builtin_inff();
+
+  __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  int bh, qt;
+  tile_of_block(p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int q0 = qt * BM, qw = q0 + 32 * w, row = qw + c;
+  int kend = Tk;
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  const int kend_wg = CAUSAL ? min(kend, q0 + BM) : kend;
+  const int ntiles = kend_wg > 0 ? (kend_wg + kBT - 1) / kBT : 0;       // tiles with any allowed key
+  const int nall = (Tk + kBT - 1) / kBT;                                // tiles to write
+
+  const int64_t qoff = (int64_t)bh * Tq * D, koff = (int64_t)bh * Tk * D;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + koff;
+  bf16x8 qf[DT];
+  load_row<D>(static_cast<const __bf16*>(p.q) + qoff, row, Tq, g, p.neg != 0, qf);
+  float l2 = kPosInf;
+  if (row < Tq) {
+    const float lse = p.lse[(int64_t)bh * Tq + row];
+    l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
+  }
+  float* wrow = p.w + ((int64_t)bh * Tq + (row < Tq ? row : 0)) * Tk;
+  const bool vec = (Tk & 3) == 0;
+
+  uint32_t src[NLD];
+  tile_src_offsets<D>(w, lane, src);
+  auto load_k = [&](int j0, char* kt) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, (uint32_t)(kend - j0) * ROWB);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) lds_dma16(kr, kt + (kBwdWaves * u + w) * 1024, src[u]);
+  };
+  int fr[DT];
+  frag_offsets<D>(c, g, fr);
+  const float cs = p.scale_log2;
+
+  // store 8 consecutive keys j .. j+7 of this lane's row
+  auto store8 = [&](int j, const f32x8& v8) __attribute__((always_inline)) {
+    if (row >= Tq) return;
+    if (vec && j + 8 <= Tk) {
+      *reinterpret_cast<f32x4*>(wrow + j) = f32x4{v8[0], v8[1], v8[2], v8[3]};
+      *reinterpret_cast<f32x4*>(wrow + j + 4) = f32x4{v8[4], v8[5], v8[6], v8[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j + e < Tk) wrow[j + e] = v8[e];
+    }
+  };
+
+  auto step = [&](int it, const char* kt) __attribute__((always_inline)) {
+    const int j0 = it * kBT;
+    const bool edge = (j0 + kBT > kend) || (CAUSAL && j0 + kBT - 1 > qw);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + fr[t]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int jb = j0 + 32 * hh + 16 * m + 8 * g;   // keys jb .. jb+7 in registers 8m .. 8m+7
+        f32x8 v8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + e], cs, -l2));
+          if (edge) {
+            bool ok = jb + e < kend;
+            if (CAUSAL) ok = ok && jb + e <= row;
+            pe = ok ? pe : 0.f;
+          }
+          v8[e] = pe;
+        }
+        store8(jb, v8);
+      }
+    }
+  };
+
+  if (ntiles > 0) load_k(0, kb0);
+  pipeline_barrier<0>();
+  for (int it0 = 0; it0 < ntiles; it0 += 2) {
+    static_for<0, 2>([&](auto U) __attribute__((always_inline)) {
+      constexpr int u = decltype(U)::value;
+      const int it = it0 + u;
+      if (it < ntiles) {
+        if (it + 1 < ntiles) load_k((it + 1) * kBT, u ? kb0 : kb1);
+        step(it, u ? kb1 : kb0);
+        pipeline_barrier<0>();
+      }
+    });
+  }
+  // tiles past the causal / padding limit of the work-group: zeros
+  const f32x8 z8 = f32x8{};
+  for (int it = ntiles; it < nall; ++it)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) store8(it * kBT + 16 * m + 8 * g, z8);
+}
+
+// ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 template <int D, bool C, bool P>
@@ -425,6 +546,27 @@ template <int D>
 static hipError_t launch_bwd_mask(const BwdParams& prm, bool causal, bool keypad, hipStream_t stream) {
   if (causal) return keypad ? launch_bwd_d<D, true, true>(prm, stream) : launch_bwd_d<D, true, false>(prm, stream);
   return keypad ? launch_bwd_d<D, false, true>(prm, stream) : launch_bwd_d<D, false, false>(prm, stream);
+}
+
+template <int D, bool C, bool P>
+static hipError_t launch_weights_d(const WtsParams& prm, hipStream_t stream) {
+  WtsParams local = prm;
+  void* args[] = {&local};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&attn_weights_kernel<D, C, P>),
+                         dim3(prm.B * prm.H * prm.n_qtiles), dim3(kBwdThreads), args, 0, stream);
+}
+
+template <int D>
+static hipError_t launch_weights_mask(const WtsParams& prm, bool causal, bool keypad, hipStream_t stream) {
+  if (causal) return keypad ? launch_weights_d<D, true, true>(prm, stream) : launch_weights_d<D, true, false>(prm, stream);
+  return keypad ? launch_weights_d<D, false, true>(prm, stream) : launch_weights_d<D, false, false>(prm, stream);
+}
+
+int weights_rows_per_block(int) { return 32 * kBwdWaves; }
+
+hipError_t launch_weights(const WtsParams& prm, int d, bool causal, bool keypad, hipStream_t stream) {
+  return d == 64 ? launch_weights_mask<64>(prm, causal, keypad, stream)
+                 : launch_weights_mask<128>(prm, causal, keypad, stream);
 }
 
 int bwd_rows_per_block(int) { return 32 * kBwdWaves; }

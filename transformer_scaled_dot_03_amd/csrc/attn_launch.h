@@ -50,6 +50,22 @@ struct BwdParams {
 int rows_per_block(DType dt, int d);
 hipError_t launch_fwd(const Params& p, DType dt, int d, bool causal, bool keypad, hipStream_t stream);
 
+// Weights output: recompute the row softmax from the forward's log-sum-exp and
+// store it as fp32 [B, H, Tq, Tk].
+struct WtsParams {
+  const void* q;
+  const void* k;
+  const float* lse;         // [B, H, Tq] from the forward
+  float* w;                 // [B, H, Tq, Tk] written in full (zeros where masked)
+  const int32_t* key_lens;
+  int B, H, Tq, Tk;
+  float scale_log2;
+  int neg;
+  int n_qtiles;
+};
+int weights_rows_per_block(int d);
+hipError_t launch_weights(const WtsParams& p, int d, bool causal, bool keypad, hipStream_t stream);
+
 // Decode (one query row per (b, head)) split over the keys: arguments of the
 // split kernel and of the merge kernel.
 struct DecParams {

@@ -110,6 +110,27 @@ def attention_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     return out, lse
 
 
+def attention_weights(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
+                      causal: bool = False, key_lens: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      weights: torch.Tensor | None = None,
+                      stream: torch.cuda.Stream | None = None):
+    """bf16 forward returning (out, weights, lse); weights fp32 [B, h, Tq, Tk] (attn_fwd_weights)."""
+    B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16,))
+    out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
+    lse = _out_like(lse, (B, h, Tq), torch.float32, q.device, "lse")
+    weights = _out_like(weights, (B, h, Tq, Tk), torch.float32, q.device, "weights")
+    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    if scale is None:
+        scale = default_scale(dk)
+    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    status = _lib.attn_fwd_weights(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(weights), B, h, Tq, Tk,
+                                   dk, dv, float(scale), mask, kl_ptr, st)
+    if status != _lib.OK:
+        raise AttentionError(status)
+    return out, weights, lse
+
+
 def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                        dout: torch.Tensor, lse: torch.Tensor, scale: float | None = None,
                        causal: bool = False, key_lens: torch.Tensor | None = None,
