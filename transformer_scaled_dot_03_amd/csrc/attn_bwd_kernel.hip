@@ -409,10 +409,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
 // work-group per 128 query rows walks all key tiles of 64: tiles inside the
 // causal / padding limit recompute S^T = K Q^T on the matrix cores (K tiles
 // double-buffered in LDS as in the dQ kernel), tiles past it are written as
-// zeros without loading anything.  Lane (c, g) stores 8 consecutive keys of
-// its row per 16-key slice (two 16-byte stores; the two lanes of a row write
-// 64 contiguous bytes), scalar stores when Tk is not a multiple of 4 or at the
-// ragged end.
+// zeros without loading anything.  The weights leave the registers through a
+// per-wave 32 x 32 fp32 LDS block (row r's 16-byte chunk k at chunk k ^ (r/2)
+// of a 128-byte row: conflict-free for the 16-byte writes of the MFMA layout
+// and for the row-wise reads), so every global store instruction writes 8
+// whole 128-byte row segments; scalar stores when Tk is not a multiple of 4 or
+// at the ragged end.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool KEYPAD>
 __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams p) {
@@ -423,6 +425,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
 
   __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
+  __shared__ __attribute__((aligned(1024))) float stage[kBwdWaves][32 * 32];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -447,8 +450,11 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
     const float lse = p.lse[(int64_t)bh * Tq + row];
     l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
   }
-  float* wrow = p.w + ((int64_t)bh * Tq + (row < Tq ? row : 0)) * Tk;
   const bool vec = (Tk & 3) == 0;
+  float* const wbh = p.w + (int64_t)bh * Tq * Tk;
+  float* const st = stage[w];
+  // row-wise store pattern: lane writes 4 keys (16 bytes) at chunk sc of rows sr + 8 i
+  const int sr = lane >> 3, sc = lane & 7;
 
   uint32_t src[NLD];
   tile_src_offsets<D>(w, lane, src);
@@ -461,16 +467,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
   frag_offsets<D>(c, g, fr);
   const float cs = p.scale_log2;
 
-  // store 8 consecutive keys j .. j+7 of this lane's row
-  auto store8 = [&](int j, const f32x8& v8) __attribute__((always_inline)) {
-    if (row >= Tq) return;
-    if (vec && j + 8 <= Tk) {
-      *reinterpret_cast<f32x4*>(wrow + j) = f32x4{v8[0], v8[1], v8[2], v8[3]};
-      *reinterpret_cast<f32x4*>(wrow + j + 4) = f32x4{v8[4], v8[5], v8[6], v8[7]};
+  // 4 keys j .. j+3 of query row r (wave-relative) to global memory
+  auto store4 = [&](int r, int j, const f32x4& v4) __attribute__((always_inline)) {
+    if (qw + r >= Tq) return;
+    float* dst = wbh + (int64_t)(qw + r) * Tk + j;
+    if (vec && j + 4 <= Tk) {
+      *reinterpret_cast<f32x4*>(dst) = v4;
     } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (j + e < Tk) wrow[j + e] = v8[e];
+      for (int e = 0; e < 4; ++e)
+        if (j + e < Tk) dst[e] = v4[e];
     }
   };
 
@@ -488,7 +494,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int jb = j0 + 32 * hh + 16 * m + 8 * g;   // keys jb .. jb+7 in registers 8m .. 8m+7
-        f32x8 v8;
+        f32x4 v4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + e], cs, -l2));
@@ -497,10 +503,21 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
             if (CAUSAL) ok = ok && jb + e <= row;
             pe = ok ? pe : 0.f;
           }
-          v8[e] = pe;
+          v4[e >> 2][e & 3] = pe;
         }
-        store8(jb, v8);
+        // block column chunks 4m + 2g and 4m + 2g + 1 of row c
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+          *reinterpret_cast<f32x4*>(st + 32 * c + 4 * ((4 * m + 2 * g + h2) ^ ((c >> 1) & 7))) = v4[h2];
       }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = sr + 8 * i;
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(st + 32 * r + 4 * (sc ^ ((r >> 1) & 7)));
+        store4(r, j0 + 32 * hh + 4 * sc, v4);
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   };
 
@@ -517,11 +534,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
       }
     });
   }
-  // tiles past the causal / padding limit of the work-group: zeros
-  const f32x8 z8 = f32x8{};
+  // tiles past the causal / padding limit of the work-group: zeros, written
+  // row-wise (16 lanes cover one row's 64 keys)
+  const f32x4 z4 = f32x4{};
   for (int it = ntiles; it < nall; ++it)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) store8(it * kBT + 16 * m + 8 * g, z8);
+    for (int i = 0; i < 8; ++i) store4((lane >> 4) + 4 * i, it * kBT + 4 * (lane & 15), z4);
 }
 
 // ---------------------------------------------------------------------------
