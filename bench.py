@@ -143,7 +143,7 @@ def time_backward(torch, tsd, w, qd, kd, vd, kld, steps, warmup):
     dout = grad_output(w.B, w.h, w.Tq, w.d, seed=0).to(dev)
     out = torch.empty_like(qd)
     lse = torch.empty((w.B, w.h, w.Tq), dtype=torch.float32, device=dev)
-    delta = torch.empty_like(lse)
+    delta = torch.empty((2, w.B, w.h, w.Tq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     rc = tsd.attn_fwd_lse(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), lse.data_ptr(),
                           w.B, w.h, w.Tq, w.Tk, w.d, w.d, w.scale, mask, klp, st)

@@ -144,8 +144,10 @@ int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* 
  *   q, k, v, out, dout : bfloat16 inputs, layout above; out and lse are what
  *                        attn_fwd_lse returned for these q, k, v, scale, mask
  *   lse                : fp32 [B, h, Tq] from attn_fwd_lse
- *   delta              : fp32 [B, h, Tq] caller-owned workspace; written with
- *                        D_i (computed from the bfloat16 out and dout)
+ *   delta              : fp32 [2, B, h, Tq] caller-owned workspace: the first
+ *                        kernel writes D_i (from the bfloat16 out and dout)
+ *                        and lse_i * log2(e) (+inf for an empty row) there,
+ *                        the second reads them; no initialisation needed
  *   dq, dk, dv         : bfloat16 outputs shaped like q, k, v (fp32
  *                        accumulation, one rounding each)
  *   other arguments    : as for attn_fwd; d_k = d_v in {64, 128}
@@ -153,8 +155,8 @@ int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* 
  * second reads delta and writes dk, dv.  Outputs may not overlap any input
  * or each other (ATTN_ERR_ALIAS).  Empty work: B or h = 0, or Tq = Tk = 0,
  * is a no-op; Tq = 0 with Tk > 0 writes zero dk, dv (q, out, dout, lse,
- * delta, dq unused); Tk = 0 with Tq > 0 writes zero dq and delta (k, v, dk,
- * dv unused).
+ * delta, dq unused); Tk = 0 with Tq > 0 writes zero dq, D = 0 and
+ * lse * log2(e) = +inf into delta (k, v, dk, dv unused).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
              const float* lse, float* delta, void* dq, void* dk, void* dv,

@@ -176,10 +176,11 @@ def test_backward_zero_sized(tsd):
     out, lse = tsd.attention_lse(q, k, v, scale=0.1)
     dout = grad_output(2, 2, 40, 128).to(DEV)
     dq = torch.full_like(q, 7.0)
-    delta = torch.full((2, 2, 40), 7.0, device=DEV)
+    delta = torch.full((2, 2, 2, 40), 7.0, device=DEV)
     tsd.attention_backward(q, k, v, out, dout, lse, scale=0.1, dq=dq, delta=delta)
     torch.cuda.synchronize()
-    assert not dq.any() and not delta.any() and torch.all(torch.isneginf(lse))
+    assert not dq.any() and not delta[0].any() and torch.all(torch.isneginf(lse))
+    assert torch.all(torch.isposinf(delta[1]))   # lse * log2(e) of an empty row
 
 
 # ---------------------------------------------------------------------------
@@ -264,9 +265,9 @@ def test_backward_writes_nothing_outside_its_outputs(tsd):
     bq, dq = guarded(q.numel(), torch.bfloat16)
     bk, dk = guarded(k.numel(), torch.bfloat16)
     bv, dv = guarded(v.numel(), torch.bfloat16)
-    bd, delta = guarded(B * H * Tq, torch.float32)
+    bd, delta = guarded(2 * B * H * Tq, torch.float32)
     tsd.attention_backward(q, k, v, out, dout, lse, scale=0.125, dq=dq.view(q.shape), dk=dk.view(k.shape),
-                           dv=dv.view(v.shape), delta=delta.view(B, H, Tq))
+                           dv=dv.view(v.shape), delta=delta.view(2, B, H, Tq))
     torch.cuda.synchronize()
     for buf in (bq, bk, bv, bd):
         assert torch.all(buf[:pad] == 3.0) and torch.all(buf[-pad:] == 3.0)

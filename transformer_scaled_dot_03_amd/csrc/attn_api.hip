@@ -129,11 +129,11 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   // written: delta, dq (rows), dk, dv (keys); read: q, k, v, out, dout, lse
   typedef unsigned __int128 u128;
   const u128 nq = rows ? (u128)bh * Tq * d_k * 2 : 0, nkv = keys ? (u128)bh * Tk * d_k * 2 : 0;
-  const u128 nr = rows ? (u128)bh * Tq * 4 : 0;
+  const u128 nr = rows ? (u128)bh * Tq * 4 : 0;   // lse; delta holds two such arrays
   const void* in_p[6] = {q, k, v, out, dout, lse};
   const u128 in_n[6] = {nq, nkv, nkv, nq, nq, nr};
   const void* out_p[4] = {delta, dq, dk, dv};
-  const u128 out_n[4] = {nr, nq, nkv, nkv};
+  const u128 out_n[4] = {2 * nr, nq, nkv, nkv};
   for (int i = 0; i < 4; ++i) {
     for (int j = 0; j < 6; ++j)
       if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIAS;

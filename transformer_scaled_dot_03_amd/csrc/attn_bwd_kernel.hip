@@ -11,10 +11,11 @@
 // training of every weight matrix).
 //
 // Two kernels, no atomics and no scratch beyond the caller's delta array:
-//   * attn_bwd_dq_kernel: one work-group per 128 query rows; writes D_i, then
-//     streams K/V tiles of 64 keys and accumulates dQ in registers;
+//   * attn_bwd_dq_kernel: one work-group per 128 query rows; writes D_i and
+//     lse_i log2(e) to the caller's workspace, then streams K/V tiles of 64
+//     keys and accumulates dQ in registers;
 //   * attn_bwd_dkdv_kernel: one work-group per 128 keys; streams Q/dO tiles of
-//     64 rows (with their lse and D) and accumulates dK, dV in registers.
+//     64 rows (with their D and lse log2(e)) and accumulates dK, dV in registers.
 // Matrix-core mapping as in the forward (v_mfma_f32_32x32x16_bf16, lane l,
 // g = l / 32, c = l % 32): products whose output rows are the lane's own
 // row/key take the streamed operand from LDS as 16-byte fragments read in
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
   if (row < Tq) {
     const float lse = p.lse[(int64_t)bh * Tq + row];
     l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
-    if (g == 0) p.delta[(int64_t)bh * Tq + row] = delta;
+    if (g == 0) {
+      p.delta[(int64_t)bh * Tq + row] = delta;
+      p.delta[(int64_t)p.B * p.H * Tq + (int64_t)bh * Tq + row] = l2;
+    }
   }
 
   uint32_t src[NLD];
@@ -217,18 +221,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, gf[t], dp, 0, 0, 0);
       }
       // register e: key j0 + 32hh + 16(e/8) + 8g + e%8 of this lane's row
+      f32x16 pr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cs, -l2));
+      if (edge) {   // one wave-uniform branch: allowed keys of this row are [0, hi)
+        const int hi = CAUSAL ? min(kend, row + 1) : kend;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+          pr[e] = key < hi ? pr[e] : 0.f;
+        }
+      }
       f32x16 ds;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], cs, -l2));
-        if (edge) {
-          const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-          bool ok = key < kend;
-          if (CAUSAL) ok = ok && key <= row;
-          pe = ok ? pe : 0.f;
-        }
-        ds[e] = pe * (dp[e] - delta);
-      }
+      for (int e = 0; e < 16; ++e) ds[e] = pr[e] * (dp[e] - delta);
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         f32x8 d8;
@@ -268,13 +274,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   using TG = BwdTile<D>;
   constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT, NO = TG::NO;
   constexpr int BK = 32 * kBwdWaves;
-  constexpr float kNegInf = -__builtin_inff(), kPosInf = __builtin_inff();
 
   __shared__ __attribute__((aligned(1024))) char qb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char qb1[TILEB];
   __shared__ __attribute__((aligned(1024))) char gb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char gb1[TILEB];
-  // per tile: lse of its 64 rows in [0, 64), D in [64, 128)
+  // per tile: lse * log2(e) of its 64 rows in [0, 64), D in [64, 128)
   __shared__ __attribute__((aligned(256))) float rb0[128];
   __shared__ __attribute__((aligned(256))) float rb1[128];
 
@@ -295,8 +300,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   const int64_t qoff = (int64_t)bh * Tq * D, koff = (int64_t)bh * Tk * D;
   const __bf16* Qg = static_cast<const __bf16*>(p.q) + qoff;
   const __bf16* Gg = static_cast<const __bf16*>(p.dout) + qoff;
-  const float* Lg = p.lse + (int64_t)bh * Tq;
-  const float* Dg = p.delta + (int64_t)bh * Tq;
+  const float* Dg = p.delta + (int64_t)bh * Tq;                                  // D
+  const float* Lg = p.delta + (int64_t)p.B * p.H * Tq + (int64_t)bh * Tq;       // lse * log2(e)
 
   // this lane's key row: K negated for a negative scale (S = scale Q K^T), and V
   bf16x8 kf[DT], vf[DT];
@@ -314,7 +319,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       lds_dma16(qr, qt + (kBwdWaves * u + w) * 1024, src[u]);
       lds_dma16(gr, gt + (kBwdWaves * u + w) * 1024, src[u]);
     }
-    // lse (wave 0) and D (wave 1) of rows r0 .. r0 + 63; rows at or past Tq read as 0
+    // lse * log2(e) (wave 0) and D (wave 1) of rows r0 .. r0 + 63; rows at or past Tq read as 0
     if (w < 2) {
       const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(w == 0 ? Lg + r0 : Dg + r0, (uint32_t)(Tq - r0) * 4);
       lds_dma4(rr, reinterpret_cast<char*>(rt) + 256 * w, 4 * lane);
@@ -354,20 +359,24 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         f32x8 p8, d8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float lse = j < 4 ? la[j] : lb[j - 4];
+          const float l2 = j < 4 ? la[j] : lb[j - 4];
           const float dlt = j < 4 ? da[j] : db[j - 4];
-          const float l2 = lse == kNegInf ? kPosInf : lse * kLog2e;
-          float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + j], cs, -l2));
-          float de = pe * (dp[8 * m + j] - dlt);
-          if (edge) {   // select, not multiply: a masked weight may be inf before it
-            const int rw = r0 + rl + j;
-            bool ok = key < kend && rw < Tq;
-            if (CAUSAL) ok = ok && key <= rw;
-            pe = ok ? pe : 0.f;
-            de = ok ? de : 0.f;
-          }
+          const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * m + j], cs, -l2));
           p8[j] = pe;
-          d8[j] = de;
+          d8[j] = pe * (dp[8 * m + j] - dlt);
+        }
+        // one wave-uniform branch for the 8 rows; select, not multiply: a masked
+        // weight may be inf before it
+        if (edge) {
+          // valid rows of this lane's key: [lo, hi) (empty for a key past the length)
+          const int lo = CAUSAL ? key : 0, hi = key < kend ? Tq : 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int rw = r0 + rl + j;
+            const bool ok = rw >= lo && rw < hi;
+            p8[j] = ok ? p8[j] : 0.f;
+            d8[j] = ok ? d8[j] : 0.f;
+          }
         }
         const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
         const bf16x8 dsb = __builtin_convertvector(d8, bf16x8);

@@ -34,7 +34,8 @@ struct BwdParams {
   const void* o;
   const void* dout;
   const float* lse;         // [B, H, Tq] from the forward
-  float* delta;             // [B, H, Tq] written: D_i = dO_i . O_i
+  float* delta;             // [2, B, H, Tq] written by the dQ kernel: D_i = dO_i . O_i, then
+                            // lse_i * log2(e) (+inf for a row with no allowed key)
   void* dq;
   void* dk;
   void* dv;

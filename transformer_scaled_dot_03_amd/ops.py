@@ -140,8 +140,8 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     """Gradients (dq, dk, dv) of attention for bf16 tensors (attn_bwd).
 
     out and lse are what attention_lse returned for these inputs; dout is the
-    gradient of the loss with respect to out.  delta (fp32 [B, h, Tq]) is the
-    kernels' workspace, allocated here when not given.
+    gradient of the loss with respect to out.  delta (fp32 [2, B, h, Tq]) is
+    the kernels' workspace, allocated here when not given.
     """
     B, h, Tq, Tk, d_k, d_v = _check_qkv(q, k, v, (torch.bfloat16,))
     for name, t, shape in (("out", out, (B, h, Tq, d_v)), ("dout", dout, (B, h, Tq, d_v))):
@@ -152,7 +152,7 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     dq = _out_like(dq, q.shape, q.dtype, q.device, "dq")
     dk = _out_like(dk, k.shape, k.dtype, k.device, "dk")
     dv = _out_like(dv, v.shape, v.dtype, v.device, "dv")
-    delta = _out_like(delta, (B, h, Tq), torch.float32, q.device, "delta")
+    delta = _out_like(delta, (2, B, h, Tq), torch.float32, q.device, "delta")
     mask, kl_ptr = _mask_args(B, causal, key_lens)
     if scale is None:
         scale = default_scale(d_k)
