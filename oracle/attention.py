@@ -43,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["allowed_mask", "attention_backward_fp64", "attention_backward_sampled_fp64", "attention_fp64",
-           "attention_lse_fp64", "softmax_rows_fp64"]
+           "attention_lse_fp64", "multi_head_attention_fp64", "softmax_rows_fp64"]
 
 
 def allowed_mask(rows: np.ndarray, Tk: int, causal: bool, key_len: int | None) -> np.ndarray:
@@ -263,3 +263,42 @@ def attention_backward_sampled_fp64(q, k, v, dout, scale: float, causal: bool = 
                 gv[b, hh] += pc.T @ gb
                 gk[b, hh] += sc * ((pc * (dp[:, keys] - d_row)).T @ qb)
     return gq, gk, gv
+
+
+def multi_head_attention_fp64(xq, xk, xv, wq, wk, wv, wo, heads: int, scale: float, causal: bool = False,
+                              key_lens=None, rows=None, batches=None):
+    """Multi-head attention in fp64, as the pages define it.
+
+        head_i = Attention(Xq W_i^Q, Xk W_i^K, Xv W_i^V),
+        MultiHead = Concat(head_1, ..., head_h) W^O
+    (notebook chapter, "Multi-Head Self-Attention"; cuijiawei.cn, "The core idea:
+    scaled dot-product attention" and its MultiHeadAttention snippet; overview
+    page, multi_head_attention()).  Read without bias terms: the formula and the
+    NumPy version have none (the PyTorch snippet's nn.Linear layers would add
+    them).  Head i uses columns i*d .. i*d+d-1 of each projection (the snippet's
+    view(B, T, h, d) of the projected rows) and rows i*d .. of W^O.
+
+    xq [B, Tq, dm], xk, xv [B, Tk, dm]; wq, wk, wv [dm, h*d]; wo [h*d, dm] (row
+    vectors times matrices, x @ W).  scale, causal, key_lens as attention_fp64.
+    rows: None or query-row indices (only those output rows); batches: None or
+    batch indices to compute (others left 0).  Returns y [B, R, dm] fp64.
+    """
+    xq = np.asarray(xq)
+    xk = np.asarray(xk)
+    xv = np.asarray(xv)
+    B, Tq, dm = xq.shape
+    Tk = xk.shape[1]
+    hd = np.asarray(wq).shape[1]
+    d = hd // heads
+    assert hd == heads * d and np.asarray(wo).shape == (hd, dm)
+    wq, wk, wv, wo = (np.asarray(w, dtype=np.float64) for w in (wq, wk, wv, wo))
+    row_idx = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = np.zeros((B, row_idx.shape[0], dm))
+    for b in (range(B) if batches is None else batches):
+        q = (xq[b].astype(np.float64) @ wq).reshape(Tq, heads, d).transpose(1, 0, 2)[None]
+        k = (xk[b].astype(np.float64) @ wk).reshape(Tk, heads, d).transpose(1, 0, 2)[None]
+        v = (xv[b].astype(np.float64) @ wv).reshape(Tk, heads, d).transpose(1, 0, 2)[None]
+        kl = None if key_lens is None else [int(np.asarray(key_lens)[b])]
+        o = attention_fp64(q, k, v, scale, causal=causal, key_lens=kl, rows=rows)[0]   # [h, R, d]
+        y[b] = o.transpose(1, 0, 2).reshape(row_idx.shape[0], hd) @ wo
+    return y
