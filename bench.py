@@ -23,6 +23,10 @@ resident in device memory before the timed region.  Prints ONE JSON line:
   weights    attn_fwd_weights on the decoder-causal workload (B16 h16 T1024
              d64): the fp32 weight matrix written per second; the weights
              kernel's time is the call's minus attn_fwd_lse's (both HIP events)
+  mha        the multi-head wrapper (attn_mha_fwd) on B32 T1024 d_model 512 h8:
+             projection GEMMs (rocBLAS) + head moves + attention + W^O GEMM;
+             TFLOP/s counts 2*B*d_model^2*(2 Tq + 2 Tk) projection flops plus the
+             attention's 4*B*h*Tq*Tk*d
   backward   (bf16 workloads) the gradient pass on the same inputs: attn_bwd
              timed with HIP events after one attn_fwd_lse; TFLOP/s counts the
              algorithmic 10*B*h*Tq*Tk*d flops (halved for causal): recomputed
@@ -296,6 +300,53 @@ def time_weights(torch, tsd, name, steps, warmup):
     }
 
 
+def time_mha(torch, tsd, name, steps, warmup):
+    """HIP-event time of attn_mha_fwd on a multi-head workload."""
+    from transformer_scaled_dot_03_amd.workloads import MHA_WORKLOADS, mha_inputs
+    c = MHA_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    xq, _, _, wq, wk, wv, wo = (t.to(dev) for t in mha_inputs(c["B"], c["Tq"], c["Tk"], c["d_model"], seed=0))
+    B, Tq, Tk, dm, h = c["B"], c["Tq"], c["Tk"], c["d_model"], c["heads"]
+    y = torch.empty_like(xq)
+    nb = tsd.attn_mha_workspace_bytes(B, Tq, Tk, dm)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    d = dm // h
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    args = (xq.data_ptr(), xq.data_ptr(), xq.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wo.data_ptr(),
+            y.data_ptr(), B, Tq, Tk, dm, h, scale, tsd.MASK_CAUSAL if c["causal"] else 0, None, ws.data_ptr(), nb,
+            stream.cuda_stream)
+
+    def mstep():
+        rc = tsd.attn_mha_fwd(*args)
+        if rc != tsd.OK:
+            raise RuntimeError(f"attn_mha_fwd failed: {tsd.attn_status_str(rc)}")
+
+    for _ in range(warmup):
+        mstep()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        mstep()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    proj = 2.0 * B * dm * dm * (2 * Tq + 2 * Tk)
+    att = 4.0 * B * h * Tq * Tk * d / (2 if c["causal"] else 1)
+    return {
+        "workload": name,
+        "what": "attn_mha_fwd: Q, K, V projections (rocBLAS), head split, attention, head merge, W^O (rocBLAS)",
+        "ms": round(ms, 4),
+        "flops_per_step": proj + att,
+        "tflops": round((proj + att) / (ms * 1e-3) / 1e12, 2),
+        "frac": round((proj + att) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "peak": PEAK_BF16_TFLOPS,
+        "steps": steps,
+    }
+
+
 def compulsory_bytes(w) -> float:
     es = 2 if w.dtype == "bf16" else 4
     return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
@@ -352,6 +403,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-weights", action="store_true", help="skip the weights-output measurement")
+    ap.add_argument("--no-mha", action="store_true", help="skip the multi-head wrapper measurement")
     ap.add_argument("--decode-workload", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -453,6 +505,8 @@ def main():
         rec["decode"] = time_decode(torch, tsd, args.decode_workload or DECODE_HEADLINE, args.steps, args.warmup)
     if not args.no_weights:
         rec["weights"] = time_weights(torch, tsd, "dec_causal_bf16_b16h16t1024d64", args.steps, args.warmup)
+    if not args.no_mha:
+        rec["mha"] = time_mha(torch, tsd, "mha_self_bf16_b32t1024dm512h8", args.steps, args.warmup)
     if not args.no_mfma_probe and w.dtype == "bf16":
         rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:

@@ -1,6 +1,7 @@
 /*
  * attn.h -- C ABI of libattn.so: fused scaled dot-product attention (forward,
- * log-sum-exp, backward, single-row decode) for AMD Instinct MI355X (gfx950).
+ * log-sum-exp, backward, weights, single-row decode, multi-head wrapper) for
+ * AMD Instinct MI355X (gfx950).
  *
  * Operation (per batch entry b and head, for every query row i):
  *
@@ -77,7 +78,8 @@ enum {
   ATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */
   ATTN_ERR_TOO_LARGE = -8,   /* more than 2^31-1 work-groups, or one head's rows of a tensor
                                 exceed 4 GiB (T * d * element size >= 2^32) */
-  ATTN_ERR_WORKSPACE = -9,   /* attn_decode: workspace NULL or smaller than attn_decode_workspace_bytes() */
+  ATTN_ERR_WORKSPACE = -9,   /* workspace NULL or smaller than the *_workspace_bytes() figure */
+  ATTN_ERR_BLAS = -10,       /* attn_mha_fwd: a rocBLAS GEMM failed (rocblas_status in attn_last_hip_error()) */
   ATTN_ERR_HIP = -100        /* the kernel launch failed; see attn_last_hip_error() */
 };
 
@@ -218,6 +220,44 @@ int attn_decode(const void* q, const void* k, const void* v, void* out,
 
 /* Bytes of workspace attn_decode needs for (B, h, Tk, d); 0 for invalid sizes. */
 size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d);
+
+/*
+ * attn_mha_fwd: multi-head attention forward,
+ *
+ *     MultiHead = Concat(head_1, ..., head_h) W^O,
+ *     head_i = Attention(Xq W_i^Q, Xk W_i^K, Xv W_i^V)
+ *
+ * ("Attention Is All You Need" notebook chapter, "Multi-Head Self-Attention";
+ * cuijiawei.cn, the MultiHeadAttention snippet: head i is columns i*d .. i*d+d-1
+ * of each projection, d = d_model / h), with Attention() the operation of
+ * attn_fwd (same scale, mask_kind and key_lens meaning).  No bias terms (the
+ * formula has none).  Self-attention passes the same pointer for xq, xk, xv.
+ *   xq      : bf16 [B, Tq, d_model];  xk, xv : bf16 [B, Tk, d_model]
+ *   wq, wk, wv : bf16 [d_model, d_model] (row vector times matrix: x W)
+ *   wo      : bf16 [d_model, d_model]
+ *   y       : bf16 [B, Tq, d_model]
+ *   h       : heads; d_model / h must be 64 or 128
+ *   workspace : caller-owned device memory of at least
+ *             attn_mha_workspace_bytes(B, Tq, Tk, d_model) bytes, 256-byte
+ *             aligned, overlapping no tensor; no initialisation needed; calls
+ *             that share it must not overlap in time
+ * The projections are rocBLAS GEMMs (bf16 operands, fp32 accumulation, bf16
+ * results: the projected Q, K, V and the merged heads are rounded to bf16),
+ * pointed at a slice of the workspace; the head moves and the attention are
+ * this library's kernels.  All work is enqueued on `stream`.  The first call
+ * on a device creates that device's rocBLAS handle (rocBLAS's own set-up),
+ * kept until the process ends; calls are serialised on it.
+ * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE and ATTN_ERR_BLAS.  B or Tq = 0
+ * is a no-op; Tk = 0 gives y = 0.
+ */
+int attn_mha_fwd(const void* xq, const void* xk, const void* xv,
+                 const void* wq, const void* wk, const void* wv, const void* wo, void* y,
+                 int B, int Tq, int Tk, int d_model, int h, float scale,
+                 int mask_kind, const int32_t* key_lens,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace attn_mha_fwd needs for (B, Tq, Tk, d_model); 0 for invalid sizes. */
+size_t attn_mha_workspace_bytes(int B, int Tq, int Tk, int d_model);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_str(int status);

@@ -40,7 +40,7 @@ def _declared_enum():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_weights", "attn_bwd", "attn_decode",
-         "attn_decode_workspace_bytes",
+         "attn_decode_workspace_bytes", "attn_mha_fwd", "attn_mha_workspace_bytes",
          "attn_status_str", "attn_last_hip_error", "attn_version"])
 
 
@@ -55,7 +55,8 @@ def test_library_exports_every_declared_symbol(L):
 def test_status_constants_match_header(L):
     enum = _declared_enum()
     assert enum["ATTN_OK"] == L.OK
-    for name in ("NULL", "SHAPE", "HEADDIM", "MASK", "ALIAS", "ALIGN", "SCALE", "TOO_LARGE", "WORKSPACE", "HIP"):
+    for name in ("NULL", "SHAPE", "HEADDIM", "MASK", "ALIAS", "ALIGN", "SCALE", "TOO_LARGE", "WORKSPACE", "BLAS",
+                 "HIP"):
         assert enum["ATTN_ERR_" + name] == getattr(L, "ERR_" + name)
     for name in ("NONE", "CAUSAL", "KEYPAD"):
         assert enum["ATTN_MASK_" + name] == getattr(L, "MASK_" + name)
@@ -63,7 +64,7 @@ def test_status_constants_match_header(L):
 
 def test_status_strings_and_version(L):
     for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_HEADDIM, L.ERR_MASK, L.ERR_ALIAS,
-                 L.ERR_ALIGN, L.ERR_SCALE, L.ERR_TOO_LARGE, L.ERR_WORKSPACE, L.ERR_HIP):
+                 L.ERR_ALIGN, L.ERR_SCALE, L.ERR_TOO_LARGE, L.ERR_WORKSPACE, L.ERR_BLAS, L.ERR_HIP):
         s = L.attn_status_str(code)
         assert s and s != "unknown status"
     assert L.attn_status_str(12345) == "unknown status"
@@ -307,6 +308,59 @@ def test_decode_bad_arguments_rejected_before_any_launch(L, over, code):
 def test_decode_empty_is_a_no_op(L):
     assert _call_dec(L, B=0, q=None, out=None, ws=None) == L.OK
     assert _call_dec(L, h=0) == L.OK
+
+
+# multi-head: fake addresses 256 MiB apart, never dereferenced
+MHA = dict(xq=0x10000000, xk=0x10000000, xv=0x10000000, wq=0x20000000, wk=0x30000000, wv=0x40000000,
+           wo=0x50000000, y=0x60000000, B=2, Tq=100, Tk=100, dm=512, h=8, scale=0.125, mask_kind=0,
+           key_lens=None, ws=0x80000000, ws_bytes=1 << 28, stream=None)
+
+
+def _call_mha(L, **over):
+    a = dict(MHA)
+    a.update(over)
+    return L.attn_mha_fwd(a["xq"], a["xk"], a["xv"], a["wq"], a["wk"], a["wv"], a["wo"], a["y"], a["B"], a["Tq"],
+                          a["Tk"], a["dm"], a["h"], a["scale"], a["mask_kind"], a["key_lens"], a["ws"],
+                          a["ws_bytes"], a["stream"])
+
+
+def test_mha_workspace_size(L):
+    assert L.attn_mha_workspace_bytes(-1, 10, 10, 512) == 0
+    assert L.attn_mha_workspace_bytes(1, 10, 10, 0) == 0
+    n = L.attn_mha_workspace_bytes(2, 100, 100, 512)
+    # projections, q, k, v, o (bf16) and the rocBLAS slice
+    assert n >= 5 * 2 * 100 * 512 * 2 + (32 << 20) and n % 256 == 0
+    assert L.attn_mha_workspace_bytes(2, 100, 300, 512) > n
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "ERR_SHAPE"),
+    (dict(h=0), "ERR_SHAPE"),
+    (dict(h=3), "ERR_SHAPE"),                 # 512 % 3 != 0
+    (dict(h=16), "ERR_HEADDIM"),              # d = 32
+    (dict(dm=96, h=1), "ERR_HEADDIM"),
+    (dict(mask_kind=4), "ERR_MASK"),
+    (dict(mask_kind=2), "ERR_MASK"),
+    (dict(scale=float("nan")), "ERR_SCALE"),
+    (dict(wq=None), "ERR_NULL"),
+    (dict(y=None), "ERR_NULL"),
+    (dict(xk=None), "ERR_NULL"),
+    (dict(ws=None), "ERR_WORKSPACE"),
+    (dict(ws_bytes=4096), "ERR_WORKSPACE"),
+    (dict(ws=0x80000010), "ERR_ALIGN"),       # the workspace needs 256 bytes
+    (dict(wo=0x50000008), "ERR_ALIGN"),
+    (dict(y=0x10000000 + 512), "ERR_ALIAS"),  # y inside xq
+    (dict(ws=0x30000000), "ERR_ALIAS"),       # workspace on wk
+    (dict(y=0x80000000 + 4096), "ERR_ALIAS"), # y inside the workspace
+])
+def test_mha_bad_arguments_rejected_before_any_launch(L, over, code):
+    assert _call_mha(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+def test_mha_empty_is_a_no_op(L):
+    assert _call_mha(L, B=0, xq=None, y=None, ws=None) == L.OK
+    assert _call_mha(L, Tq=0) == L.OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -1,0 +1,115 @@
+"""GPU parity of the multi-head attention forward (attn_mha_fwd) against the fp64 oracle.
+
+The oracle (multi_head_attention_fp64) projects, attends and re-projects in
+fp64 on exactly the bf16 inputs and weights the GPU sees.  The GPU path rounds
+the projected Q, K, V, the attention output and the merged heads to bf16 (each
+stage a 2^-9 relative rounding) and accumulates every product in fp32.  An
+emulation of these roundings on the CPU, with unit-variance inputs and weights
+~ N(0, 1/d_model), gives a per-row ||err||/||ref|| of at most 5.4e-3 and a
+max |err| / max |ref| of at most 4.3e-3; the gate is 2e-2 on both.  (With
+inputs scaled x4 the softmax becomes so peaked that rounding the projected Q, K
+to bf16 moves the result by ~3e-2: outside this gate, and not tested here.)
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import multi_head_attention_fp64
+from transformer_scaled_dot_03_amd.workloads import MHA_WORKLOADS, mha_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ROW_REL = 2e-2
+MAX_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def tsd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_scaled_dot_03_amd as m
+    m.raw_library()  # fail loudly if the HIP library is missing
+    return m
+
+
+def _f(t):
+    return t.float().cpu().numpy()
+
+
+def assert_mha(got, want, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == want.shape and np.all(np.isfinite(got)), what
+    err = got - want
+    rn = np.linalg.norm(want, axis=-1)
+    en = np.linalg.norm(err, axis=-1)
+    row = float((en / np.where(rn > 0, rn, 1.0)).max())
+    mx = float(np.abs(err).max() / max(np.abs(want).max(), 1e-30))
+    print(f"[mha parity] {what}: max row rel {row:.3e}, max|err|/max|ref| {mx:.3e}", flush=True)
+    assert row <= ROW_REL and mx <= MAX_REL, f"{what}: row rel {row:.3e}, max ratio {mx:.3e}"
+
+
+def _run_check(tsd, B, Tq, Tk, dm, h, causal=False, key_lens=None, cross=False, seed=0):
+    xq, xk, xv, wq, wk, wv, wo = mha_inputs(B, Tq, Tk, dm, seed=seed, cross=cross)
+    d = dm // h
+    scale = float(np.float32(d ** -0.5))
+    kl = None if key_lens is None else torch.tensor(key_lens, dtype=torch.int32).to(DEV)
+    dv = [t.to(DEV) for t in (xq, xk, xv, wq, wk, wv, wo)]
+    y = tsd.multi_head_attention(dv[0], *dv[3:], h, xk=dv[1], xv=dv[2], scale=scale, causal=causal, key_lens=kl)
+    torch.cuda.synchronize()
+    want = multi_head_attention_fp64(_f(xq), _f(xk), _f(xv), _f(wq), _f(wk), _f(wv), _f(wo), h, scale,
+                                     causal=causal, key_lens=key_lens)
+    assert_mha(_f(y), want, f"mha B{B} Tq{Tq} Tk{Tk} dm{dm} h{h} causal={causal} keypad={key_lens is not None}")
+    return y
+
+
+@pytest.mark.parametrize("dm,h", [(512, 8), (256, 2), (512, 4)])
+@pytest.mark.parametrize("mask", ["none", "causal", "keypad"])
+def test_mha_self_attention(tsd, dm, h, mask):
+    T = 200
+    _run_check(tsd, 2, T, T, dm, h, causal=mask == "causal", key_lens=[120, T] if mask == "keypad" else None)
+
+
+@pytest.mark.parametrize("Tq,Tk", [(77, 130), (1, 300), (130, 65)])
+def test_mha_cross_attention(tsd, Tq, Tk):
+    _run_check(tsd, 3, Tq, Tk, 512, 8, cross=True, seed=Tq + Tk)
+    _run_check(tsd, 2, Tq, Tk, 256, 2, cross=True, key_lens=[Tk // 2, Tk + 1], seed=Tq)
+
+
+def test_mha_no_keys_gives_zeros_and_small_workspace_is_rejected(tsd):
+    xq, xk, xv, wq, wk, wv, wo = mha_inputs(2, 10, 0, 256, seed=3, cross=True)
+    dv = [t.to(DEV) for t in (xq, xk, xv, wq, wk, wv, wo)]
+    y = tsd.multi_head_attention(dv[0], *dv[3:], 4, xk=dv[1], xv=dv[2])
+    torch.cuda.synchronize()
+    assert not y.any()
+    xq, xk, xv, wq, wk, wv, wo = (t.to(DEV) for t in mha_inputs(1, 16, 16, 256, seed=4))
+    with pytest.raises(tsd.AttentionError) as e:
+        tsd.multi_head_attention(xq, wq, wk, wv, wo, 4, workspace=torch.empty(1024, dtype=torch.uint8, device=DEV))
+    assert e.value.status == tsd.ERR_WORKSPACE
+
+
+def test_mha_deterministic(tsd):
+    xq, xk, xv, wq, wk, wv, wo = (t.to(DEV) for t in mha_inputs(2, 128, 128, 512, seed=5))
+    a = tsd.multi_head_attention(xq, wq, wk, wv, wo, 8)
+    b = tsd.multi_head_attention(xq, wq, wk, wv, wo, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", list(MHA_WORKLOADS))
+def test_mha_workload(tsd, name):
+    """The full workload on the GPU; the oracle checks batch entries 0 and B-1 in full."""
+    c = MHA_WORKLOADS[name]
+    xq, xk, xv, wq, wk, wv, wo = mha_inputs(c["B"], c["Tq"], c["Tk"], c["d_model"], seed=0)
+    dv = [t.to(DEV) for t in (xq, wq, wk, wv, wo)]
+    d = c["d_model"] // c["heads"]
+    scale = float(np.float32(d ** -0.5))
+    y = tsd.multi_head_attention(dv[0], *dv[1:], c["heads"], scale=scale, causal=c["causal"])
+    torch.cuda.synchronize()
+    sel = [0, c["B"] - 1]
+    want = multi_head_attention_fp64(_f(xq[sel]), _f(xk[sel]), _f(xv[sel]), _f(wq), _f(wk), _f(wv), _f(wo),
+                                     c["heads"], scale, causal=c["causal"])
+    assert_mha(_f(y[sel]), want, name)

@@ -27,6 +27,7 @@ ERR_ALIGN = -6
 ERR_SCALE = -7
 ERR_TOO_LARGE = -8
 ERR_WORKSPACE = -9
+ERR_BLAS = -10
 ERR_HIP = -100
 
 # names and C signatures of every exported entry point (kept in step with attn.h)
@@ -40,6 +41,8 @@ SIGNATURES = {
     "attn_fwd_f32": (_I, _FWD_ARGS),
     "attn_fwd_lse": (_I, _FWD_LSE_ARGS),
     "attn_bwd": (_I, _BWD_ARGS),
+    "attn_mha_fwd": (_I, [_P] * 8 + [_I] * 5 + [ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]),
+    "attn_mha_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_fwd_weights": (_I, [_P] * 6 + [_I] * 6 + [ctypes.c_float, _I, _P, _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
@@ -106,6 +109,18 @@ def attn_fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, 
     """bf16 forward plus fp32 log-sum-exp and fp32 attention weights (attn.h `attn_fwd_weights`)."""
     return raw_library().attn_fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, mask_kind,
                                           key_lens, stream)
+
+
+def attn_mha_fwd(xq, xk, xv, wq, wk, wv, wo, y, B, Tq, Tk, d_model, h, scale, mask_kind, key_lens, workspace,
+                 workspace_bytes, stream) -> int:
+    """bf16 multi-head attention forward (attn.h `attn_mha_fwd`)."""
+    return raw_library().attn_mha_fwd(xq, xk, xv, wq, wk, wv, wo, y, B, Tq, Tk, d_model, h, scale, mask_kind,
+                                      key_lens, workspace, workspace_bytes, stream)
+
+
+def attn_mha_workspace_bytes(B, Tq, Tk, d_model) -> int:
+    """Workspace bytes attn_mha_fwd needs (attn.h `attn_mha_workspace_bytes`)."""
+    return raw_library().attn_mha_workspace_bytes(B, Tq, Tk, d_model)
 
 
 def attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace, workspace_bytes,

@@ -20,7 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_api.hip"]
+SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_mha.hip", "attn_api.hip"]
+# libraries each target links (the multi-head wrapper's projections are rocBLAS GEMMs)
+LINK = {"libattn.so": ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]}
 # measurement aid for the benchmark: pure matrix-core loop (include/mfma_probe.h)
 PROBE_LIB_PATH = os.path.join(PKG, "libmfma_probe.so")
 PROBE_SOURCES = ["mfma_probe.hip"]
@@ -54,7 +56,8 @@ def _build_one(lib_path: str, sources: list[str], verbose: bool, extra_flags: li
     srcs = [os.path.join(CSRC, s) for s in sources]
     fd, tmp = tempfile.mkstemp(prefix=".lib.", suffix=".so.tmp", dir=PKG)
     os.close(fd)
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp,
+           *LINK.get(os.path.basename(lib_path), [])]
     try:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:

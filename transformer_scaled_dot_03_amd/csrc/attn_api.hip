@@ -84,6 +84,7 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
   p.n_qtiles = static_cast<int>(n_qtiles);
   p.n_wg = static_cast<int>(n_wg);
   p.lse = lse;
+  attn::set_dense_strides(p, d_k);
   const hipError_t e = attn::launch_fwd(p, dt, d_k, causal, keypad, stream);
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int>(e);
@@ -222,6 +223,91 @@ int fwd_weights(const void* q, const void* k, const void* v, void* out, float* l
   return ATTN_OK;
 }
 
+int mha_fwd(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk, const void* wv,
+            const void* wo, void* y, int B, int Tq, int Tk, int d_model, int h, float scale, int mask_kind,
+            const int32_t* key_lens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || Tq < 0 || Tk < 0 || d_model <= 0 || h <= 0 || d_model % h != 0) return ATTN_ERR_SHAPE;
+  const int d = d_model / h;
+  if (d != 64 && d != 128) return ATTN_ERR_HEADDIM;
+  if (mask_kind & ~(ATTN_MASK_CAUSAL | ATTN_MASK_KEYPAD)) return ATTN_ERR_MASK;
+  const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
+  const bool keypad = (mask_kind & ATTN_MASK_KEYPAD) != 0;
+  if (keypad && key_lens == nullptr) return ATTN_ERR_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || Tq == 0) return ATTN_OK;
+  const void* ptrs[6] = {xq, wq, wk, wv, wo, y};
+  for (const void* p : ptrs)
+    if (p == nullptr) return ATTN_ERR_NULL;
+  if (Tk > 0 && (xk == nullptr || xv == nullptr)) return ATTN_ERR_NULL;
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  for (const void* p : ptrs)
+    if (misaligned(p, 16)) return ATTN_ERR_ALIGN;
+  if (misaligned(workspace, 256) || (Tk > 0 && (misaligned(xk, 16) || misaligned(xv, 16))))
+    return ATTN_ERR_ALIGN;
+  if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
+  // rocBLAS takes 32-bit sizes; one head's rows (stride up to 3 d_model) sit behind a 32-bit range
+  const int64_t tmax = Tq > Tk ? Tq : Tk;
+  if (static_cast<int64_t>(B) * tmax * 3 * d_model > 0x7fffffffLL || tmax * 3 * d_model * 2 > 0xffffffffLL)
+    return ATTN_ERR_TOO_LARGE;
+  const int64_t bm = attn::rows_per_block(attn::DType::BF16, d);
+  const int64_t n_qtiles = (Tq + bm - 1) / bm;
+  if (static_cast<int64_t>(B) * h * n_qtiles > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
+  const attn::MhaLayout L = attn::mha_layout(B, Tq, Tk, d_model);
+  if (workspace_bytes < L.bytes) return ATTN_ERR_WORKSPACE;
+
+  typedef unsigned __int128 u128;
+  const u128 row = (u128)d_model * 2, hw = (u128)d_model * d_model * 2;
+  const u128 nxq = (u128)B * Tq * row, nxkv = (u128)B * Tk * row, ny = nxq, nw = L.bytes;
+  const void* in_p[7] = {xq, xk, xv, wq, wk, wv, wo};
+  const u128 in_n[7] = {nxq, nxkv, nxkv, hw, hw, hw, hw};
+  for (int j = 0; j < 7; ++j)
+    if (overlaps(y, ny, in_p[j], in_n[j]) || overlaps(workspace, nw, in_p[j], in_n[j])) return ATTN_ERR_ALIAS;
+  if (overlaps(y, ny, workspace, nw)) return ATTN_ERR_ALIAS;
+
+  attn::MhaArgs a;
+  a.xq = xq;
+  a.xk = xk;
+  a.xv = xv;
+  a.wq = wq;
+  a.wk = wk;
+  a.wv = wv;
+  a.wo = wo;
+  a.y = y;
+  a.workspace = workspace;
+  a.B = B;
+  a.Tq = Tq;
+  a.Tk = Tk;
+  a.d_model = d_model;
+  a.H = h;
+  a.D = d;
+  a.causal = causal;
+  a.keypad = keypad;
+  a.fused_qkv = (xq == xk && xk == xv && Tq == Tk);
+  attn::Params& p = a.attn;     // pointers and strides are set by mha_run for the chosen layout
+  p.key_lens = keypad ? key_lens : nullptr;
+  p.B = B;
+  p.H = h;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.scale_log2 = scale_log2(scale);
+  p.neg = scale < 0.f ? 1 : 0;
+  p.n_qtiles = static_cast<int>(n_qtiles);
+  p.n_wg = static_cast<int>(static_cast<int64_t>(B) * h * n_qtiles);
+  p.lse = nullptr;
+  int blas_status = 0;
+  hipError_t hip_status = hipSuccess;
+  const int r = attn::mha_run(a, stream, &blas_status, &hip_status);
+  if (r == -2) {
+    g_last_hip_error = blas_status;
+    return ATTN_ERR_BLAS;
+  }
+  if (r != 0) {
+    g_last_hip_error = static_cast<int>(hip_status);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 // workspace layout of attn_decode: partial outputs, then partial (max, sum)
 struct DecodeWorkspace {
   int n_split, keys_per_split;
@@ -296,6 +382,18 @@ int decode(const void* q, const void* k, const void* v, void* out, int B, int h,
 
 extern "C" {
 
+size_t attn_mha_workspace_bytes(int B, int Tq, int Tk, int d_model) {
+  if (B < 0 || Tq < 0 || Tk < 0 || d_model <= 0) return 0;
+  return attn::mha_layout(B, Tq, Tk, d_model).bytes;
+}
+
+int attn_mha_fwd(const void* xq, const void* xk, const void* xv, const void* wq, const void* wk, const void* wv,
+                 const void* wo, void* y, int B, int Tq, int Tk, int d_model, int h, float scale, int mask_kind,
+                 const int32_t* key_lens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mha_fwd(xq, xk, xv, wq, wk, wv, wo, y, B, Tq, Tk, d_model, h, scale, mask_kind, key_lens, workspace,
+                 workspace_bytes, stream);
+}
+
 int attn_fwd_weights(const void* q, const void* k, const void* v, void* out, float* lse, float* weights, int B,
                      int h, int Tq, int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
                      hipStream_t stream) {
@@ -353,6 +451,7 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_BLAS: return "rocBLAS GEMM failed (see attn_last_hip_error for the rocblas_status)";
     case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";

@@ -145,10 +145,13 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
   const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
 
-  const __bf16* Qg = static_cast<const __bf16*>(p.q) + (int64_t)bh * Tq * D;
-  const __bf16* Kg = static_cast<const __bf16*>(p.k) + (int64_t)bh * Tk * D;
-  const __bf16* Vg = static_cast<const __bf16*>(p.v) + (int64_t)bh * Tk * D;
-  __bf16* Og = static_cast<__bf16*>(p.o) + (int64_t)bh * Tq * D;
+  // tensors addressed through (batch, head, row) strides; rows are d contiguous elements
+  const int head = bh - b * p.H;
+  const __bf16* Qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + head * p.q_sh;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + b * p.k_sb + head * p.k_sh;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + b * p.v_sb + head * p.v_sh;
+  __bf16* Og = static_cast<__bf16*>(p.o) + b * p.o_sb + head * p.o_sh;
+  const uint32_t krs = 2u * p.k_sr, vrs = 2u * p.v_sr;    // row strides in bytes
 
   // Q rows -> registers (B operand of S^T); d index of step t is 16t + 8g + e.
   bf16x8 qf[RG][DT];
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   for (int r = 0; r < RG; ++r) {
     const int row = qw + 32 * r + c;
     const bool ok = row < Tq;
-    const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * D + 8 * g;
+    const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * p.q_sr + 8 * g;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
@@ -172,17 +175,19 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     const int pos = (WAVES * u + w) * 1024 + 16 * lane;
     const int r = pos / ROWB, pc = (pos % ROWB) / 16;
     const int key = (r & ~31) + sigma32(r & 31);
-    k_src[u] = key * ROWB + 16 * (pc ^ k_swz<D>(r));
-    v_src[u] = r * ROWB + 16 * (pc ^ v_swz<D>(r));
+    k_src[u] = key * krs + 16 * (pc ^ k_swz<D>(r));
+    v_src[u] = r * vrs + 16 * (pc ^ v_swz<D>(r));
   }
-  // rows at or past kend read as zero (buffer range check)
+  // rows at or past kend read as zero: the range ends with the last valid row's d elements
   auto load_k = [&](int j0, char* kt) {
-    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, (uint32_t)(kend - j0) * ROWB);
+    const __amdgpu_buffer_rsrc_t kr =
+        buffer_rsrc(Kg + (int64_t)j0 * p.k_sr, (uint32_t)(kend - j0 - 1) * krs + ROWB);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) lds_dma16(kr, kt + (WAVES * u + w) * 1024, k_src[u]);
   };
   auto load_v = [&](int j0, char* vt) {
-    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, (uint32_t)(kend - j0) * ROWB);
+    const __amdgpu_buffer_rsrc_t vr =
+        buffer_rsrc(Vg + (int64_t)j0 * p.v_sr, (uint32_t)(kend - j0 - 1) * vrs + ROWB);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) lds_dma16(vr, vt + (WAVES * u + w) * 1024, v_src[u]);
   };
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
           l_tot > 0.f ? 0.69314718055994531f * (base[r] + __builtin_log2f(l_tot)) : kNegInf;
     if (row < Tq) {
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-      __bf16* op = Og + (int64_t)row * D + (D / 2) * g;
+      __bf16* op = Og + (int64_t)row * p.o_sr + (D / 2) * g;
 #pragma unroll
       for (int i = 0; i < NO; ++i) {
 #pragma unroll

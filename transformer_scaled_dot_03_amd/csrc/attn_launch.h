@@ -24,7 +24,21 @@ struct Params {
   int n_qtiles;             // ceil(Tq / rows_per_block(dt, d))
   int n_wg;                 // B * H * n_qtiles work-groups
   float* lse;               // optional fp32 [B, H, Tq]: natural-log row normaliser (bf16 path)
+  // Element strides of batch entry, head and row for each tensor (the bf16
+  // kernel honours them; the dense [B, H, T, d] layout has row = d, head = T d,
+  // batch = H T d, and is what the fp32 kernel assumes).
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sr, k_sr, v_sr, o_sr;
 };
+
+// fills the strides of the dense [B, H, T, d] layout
+inline void set_dense_strides(Params& p, int d) {
+  p.q_sr = p.k_sr = p.v_sr = p.o_sr = d;
+  p.q_sh = p.o_sh = static_cast<int64_t>(p.Tq) * d;
+  p.k_sh = p.v_sh = static_cast<int64_t>(p.Tk) * d;
+  p.q_sb = p.o_sb = p.q_sh * p.H;
+  p.k_sb = p.v_sb = p.k_sh * p.H;
+}
 
 // Backward pass arguments (bf16 tensors, fp32 lse and delta).
 struct BwdParams {
@@ -66,6 +80,33 @@ struct WtsParams {
 };
 int weights_rows_per_block(int d);
 hipError_t launch_weights(const WtsParams& p, int d, bool causal, bool keypad, hipStream_t stream);
+
+// Multi-head attention forward (projections through rocBLAS, attention here,
+// reading the projections in place through strides).  Workspace layout, byte
+// offsets from its start.
+constexpr size_t kMhaBlasWorkspace = size_t(32) << 20;   // handed to rocBLAS
+struct MhaLayout {
+  size_t wcat;        // bf16 [d_model, 3 d_model]: [Wq | Wk | Wv] (self-attention)
+  size_t proj;        // bf16: [B T, 3 d_model] (self) or [B Tq, d_model] + [B Tk, 2 d_model] (cross)
+  size_t o;           // bf16 [B, Tq, h, d]: the attention output, heads side by side
+  size_t blas;        // rocBLAS workspace
+  size_t blas_bytes;
+  size_t bytes;       // total
+};
+MhaLayout mha_layout(int B, int Tq, int Tk, int d_model);
+struct MhaArgs {
+  const void *xq, *xk, *xv;   // bf16 [B, Tq, dm], [B, Tk, dm], [B, Tk, dm]
+  const void *wq, *wk, *wv;   // bf16 [dm, h d]
+  const void* wo;             // bf16 [h d, dm]
+  void* y;                    // bf16 [B, Tq, dm]
+  void* workspace;
+  int B, Tq, Tk, d_model, H, D;
+  bool causal, keypad;
+  bool fused_qkv;             // xq == xk == xv: one projection GEMM with [Wq | Wk | Wv]
+  Params attn;                // scale, mask and tiling of the attention launch
+};
+// 0 on success; -1: a HIP launch failed (*hip_status); -2: rocBLAS failed (*blas_status)
+int mha_run(const MhaArgs& a, hipStream_t stream, int* blas_status, hipError_t* hip_status);
 
 // Decode (one query row per (b, head)) split over the keys: arguments of the
 // split kernel and of the merge kernel.

@@ -212,3 +212,49 @@ def decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: f
     if status != _lib.OK:
         raise AttentionError(status)
     return out
+
+
+def multi_head_attention(xq: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, wv: torch.Tensor,
+                         wo: torch.Tensor, heads: int, xk: torch.Tensor | None = None,
+                         xv: torch.Tensor | None = None, scale: float | None = None, causal: bool = False,
+                         key_lens: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                         workspace: torch.Tensor | None = None,
+                         stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Concat(head_1..head_h) W^O with head_i = Attention(xq W_i^Q, xk W_i^K, xv W_i^V) (attn_mha_fwd).
+
+    xq: [B, Tq, d_model]; xk, xv: [B, Tk, d_model] (default: xq, i.e. self-attention);
+    wq, wk, wv, wo: [d_model, d_model]; all bf16 device tensors.  scale defaults
+    to 1/sqrt(d_model / heads).  workspace: optional uint8 device tensor of at
+    least attn_mha_workspace_bytes(B, Tq, Tk, d_model) bytes.
+    """
+    xk = xq if xk is None else xk
+    xv = xk if xv is None else xv
+    ts = (("xq", xq), ("xk", xk), ("xv", xv), ("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo))
+    for name, t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+    if xq.dim() != 3 or xk.dim() != 3 or xv.shape != xk.shape:
+        raise ValueError("xq must be [B, Tq, d_model] and xk, xv [B, Tk, d_model]")
+    B, Tq, dm = xq.shape
+    Tk = xk.shape[1]
+    if xk.shape[0] != B or xk.shape[2] != dm:
+        raise ValueError("xk, xv must be [B, Tk, d_model] with the batch and width of xq")
+    for name, w in (("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo)):
+        if tuple(w.shape) != (dm, dm):
+            raise ValueError(f"{name} must be [d_model, d_model]")
+    out = _out_like(out, (B, Tq, dm), torch.bfloat16, xq.device, "out")
+    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    need = _lib.attn_mha_workspace_bytes(B, Tq, Tk, dm)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    if scale is None:
+        scale = default_scale(dm // heads) if heads > 0 and dm % heads == 0 else 1.0
+    st = (stream if stream is not None else torch.cuda.current_stream(xq.device)).cuda_stream
+    status = _lib.attn_mha_fwd(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(out),
+                               B, Tq, Tk, dm, heads, float(scale), mask, kl_ptr, _ptr(workspace),
+                               workspace.numel(), st)
+    if status != _lib.OK:
+        raise AttentionError(status)
+    return out

@@ -137,6 +137,37 @@ def grad_output(B, h, Tq, dv, dtype="bf16", seed=0):
     return x.to(TORCH_DTYPES[dtype]).contiguous()
 
 
+# multi-head attention (projections + attention + W^O) at the base model's width:
+# d_model 512, 8 heads of 64 (notebook chapter, "Multi-Head Self-Attention")
+MHA_WORKLOADS = {
+    "mha_self_bf16_b32t1024dm512h8": dict(B=32, Tq=1024, Tk=1024, d_model=512, heads=8, causal=False),
+}
+
+
+def mha_inputs(B, Tq, Tk, d_model, seed=0, cross=False):
+    """(xq, xk, xv, wq, wk, wv, wo) for multi-head attention, bf16 on the CPU.
+
+    Recipe: g = torch.Generator('cpu').manual_seed(seed); xq [B, Tq, d_model]
+    ~ N(0, 1); when `cross`, xk [B, Tk, d_model] ~ N(0, 1) and xv likewise,
+    else xk = xv = xq (self-attention, Tk = Tq); then wq, wk, wv, wo, each
+    [d_model, d_model] ~ N(0, 1) / sqrt(d_model) (random-init weights that keep
+    the projected rows at unit variance); one round-to-nearest-even cast to bf16.
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    xq = torch.randn((B, Tq, d_model), generator=g, dtype=torch.float32)
+    if cross:
+        xk = torch.randn((B, Tk, d_model), generator=g, dtype=torch.float32)
+        xv = torch.randn((B, Tk, d_model), generator=g, dtype=torch.float32)
+    else:
+        xk = xv = xq
+    ws = [torch.randn((d_model, d_model), generator=g, dtype=torch.float32) / d_model ** 0.5 for _ in range(4)]
+    bf = lambda t: t.to(torch.bfloat16).contiguous()
+    xq_b = bf(xq)
+    xk_b = xq_b if xk is xq else bf(xk)
+    xv_b = xq_b if xv is xq else bf(xv)
+    return (xq_b, xk_b, xv_b, *(bf(w) for w in ws))
+
+
 def random_inputs(B, h, Tq, Tk, d, dtype="bf16", seed=0, qk_mul=1.0, dv=None):
     """Same recipe for an ad-hoc shape (edge-case tests); d_v defaults to d."""
     dv = d if dv is None else dv
