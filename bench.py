@@ -337,7 +337,7 @@ def time_mha(torch, tsd, name, steps, warmup):
     att = 4.0 * B * h * Tq * Tk * d / (2 if c["causal"] else 1)
     return {
         "workload": name,
-        "what": "attn_mha_fwd: Q, K, V projections (rocBLAS), head split, attention, head merge, W^O (rocBLAS)",
+        "what": "attn_mha_fwd: fused QKV projection (rocBLAS), strided attention, W^O projection (rocBLAS)",
         "ms": round(ms, 4),
         "flops_per_step": proj + att,
         "tflops": round((proj + att) / (ms * 1e-3) / 1e12, 2),

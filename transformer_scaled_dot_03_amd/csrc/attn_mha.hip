@@ -30,6 +30,23 @@
 
 namespace attn {
 
+// [Wq | Wk | Wv]: dst row r = (wq row r, wk row r, wv row r); 16 bytes per thread
+constexpr int kCatThreads = 256;
+__global__ __launch_bounds__(kCatThreads) void attn_concat3_kernel(const __bf16* __restrict__ w0,
+                                                                  const __bf16* __restrict__ w1,
+                                                                  const __bf16* __restrict__ w2,
+                                                                  __bf16* __restrict__ dst, int rows, int cols) {
+  const int c8 = cols / 8;
+  const int64_t i = (int64_t)blockIdx.x * kCatThreads + threadIdx.x;   // over rows x 3 x c8, in dst order
+  if (i >= (int64_t)rows * 3 * c8) return;
+  const int c = (int)(i % c8);
+  const int64_t rk = i / c8;
+  const int k = (int)(rk % 3);
+  const int64_t r = rk / 3;
+  const __bf16* src = k == 0 ? w0 : (k == 1 ? w1 : w2);
+  *reinterpret_cast<uint4*>(dst + i * 8) = *reinterpret_cast<const uint4*>(src + r * cols + 8 * c);
+}
+
 // ---------------------------------------------------------------------------
 // rocBLAS: one handle per device, created on first use
 // ---------------------------------------------------------------------------
@@ -97,14 +114,21 @@ int mha_run(const MhaArgs& a, hipStream_t stream, int* blas_status, hipError_t* 
   if (st != rocblas_status_success) return fail_blas(st);
 
   const int dm = a.d_model, D = a.D;
-  const size_t rowb = static_cast<size_t>(dm) * 2;
   __bf16* proj = reinterpret_cast<__bf16*>(ws + L.proj);
   Params p = a.attn;
   if (a.fused_qkv) {
     // [Wq | Wk | Wv] side by side, then one GEMM: each projected row holds q, k, v of every head
-    for (int i = 0; i < 3; ++i) {
-      const void* w = i == 0 ? a.wq : (i == 1 ? a.wk : a.wv);
-      he = hipMemcpy2DAsync(ws + L.wcat + i * rowb, 3 * rowb, w, rowb, rowb, dm, hipMemcpyDeviceToDevice, stream);
+    {
+      const __bf16* w0 = static_cast<const __bf16*>(a.wq);
+      const __bf16* w1 = static_cast<const __bf16*>(a.wk);
+      const __bf16* w2 = static_cast<const __bf16*>(a.wv);
+      __bf16* dst = reinterpret_cast<__bf16*>(ws + L.wcat);
+      int rows = dm, cols = dm;
+      void* args[] = {&w0, &w1, &w2, &dst, &rows, &cols};
+      const int64_t n = static_cast<int64_t>(dm) * 3 * (dm / 8);
+      he = hipLaunchKernel(reinterpret_cast<const void*>(&attn_concat3_kernel),
+                           dim3(static_cast<unsigned>((n + kCatThreads - 1) / kCatThreads)), dim3(kCatThreads), args,
+                           0, stream);
       if (he != hipSuccess) return fail_hip(he);
     }
     st = gemm_rowmajor(hd, a.B * a.Tq, 3 * dm, dm, a.xq, dm, ws + L.wcat, 3 * dm, proj, 3 * dm);
