@@ -256,8 +256,8 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   // mask (edge tiles only; the test is wave uniform), running max with lazy
   // rescale; masked scores become -inf and, since cs > 0, exp2 gives them
   // exactly zero weight
-  auto mask_and_rescale = [&](int j0, f32x16 (&sc)[RG][NH]) {
-    if ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw)) {
+  auto mask_and_rescale = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) {
+    if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
 #pragma unroll
       for (int r = 0; r < RG; ++r)
 #pragma unroll
@@ -343,7 +343,10 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     // staged one tile ahead of V: step j reads K(j+1) and V(j) and prefetches
     // K(j+NBUF) and V(j+NBUF-1).
     f32x16 s2[2][RG][NH];
-    auto step = [&](int it, auto U) {
+    // MASKED: the tile may hold masked keys for some row of the work-group
+    // (the interior steps carry no mask code, so the scores of the next tile
+    // and this tile's row maxima share one basic block)
+    auto step = [&](int it, auto U, auto MASKED) {
       constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
       f32x16 (&sc)[RG][NH] = s2[u & 1];
       f32x16 (&sn)[RG][NH] = s2[(u + 1) & 1];
@@ -352,9 +355,10 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
       if (it + NBUF - 1 < ntiles)
         load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
       if (it < ntw) {
-        mask_and_rescale(j0, sc);
-        // scores of the next tile (unused past the wave's last tile)
+        // scores of the next tile (unused past the wave's last tile): the
+        // matrix cores work on them while the vector ALUs take this tile's max
         scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+        mask_and_rescale(j0, sc, MASKED);
         bf16x8 pk[RG][NH][2];
         probabilities(sc, pk);
         pv(vbuf(std::integral_constant<int, u>{}), pk);
@@ -382,9 +386,18 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     pipeline_barrier<0>();
     if (ntw > 0) scores(kb0, s2[0]);
     pipeline_barrier<0>();             // K(0) consumed: its buffer takes K(NBUF)
-    for (int it0 = 0; it0 < ntiles; it0 += UNR) {
+    // tiles [0, nint) hold no masked key for any row of the work-group: keys
+    // below kend and (causal) below its first row; a multiple of UNR, so the
+    // masked loop starts on buffer 0
+    int nint = kend / BN;
+    if (CAUSAL) nint = min(nint, (q0 + 1) / BN);
+    nint = min(nint, ntiles) / UNR * UNR;
+    for (int it0 = 0; it0 < nint; it0 += UNR) {
+      static_for<0, UNR>([&](auto U) { step(it0 + U, U, std::false_type{}); });
+    }
+    for (int it0 = nint; it0 < ntiles; it0 += UNR) {
       static_for<0, UNR>([&](auto U) {
-        if (it0 + U < ntiles) step(it0 + U, U);
+        if (it0 + U < ntiles) step(it0 + U, U, std::true_type{});
       });
     }
   } else {
@@ -400,7 +413,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
       if (it < ntw) {
         f32x16 sc[RG][NH];
         scores(kbuf(std::integral_constant<int, u>{}), sc);
-        mask_and_rescale(j0, sc);
+        mask_and_rescale(j0, sc, std::true_type{});
         bf16x8 pk[RG][NH][2];
         probabilities(sc, pk);
         pv(vbuf(std::integral_constant<int, u>{}), pk);
