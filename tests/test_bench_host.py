@@ -1,0 +1,40 @@
+"""Host-side checks of bench.py's contract (no GPU needed)."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_flop_and_byte_counts():
+    sys.path.insert(0, ROOT)
+    import bench
+    from transformer_scaled_dot_03_amd.workloads import WORKLOADS
+    w = WORKLOADS["long_bf16_b1h16t16384d128"]
+    assert bench.flops_per_step(w) == 4.0 * 16 * 16384 * 16384 * 128
+    assert bench.flops_per_step(WORKLOADS["long_causal_bf16_b1h16t16384d128"]) == bench.flops_per_step(w) / 2
+    assert bench.bwd_flops_per_step(w) == 2.5 * bench.flops_per_step(w)
+    assert bench.compulsory_bytes(w) == 2 * 16 * (2 * 16384 * 128 + 2 * 16384 * 128)
+    d = WORKLOADS["decode_bf16_b8h16k16384d128"]
+    assert bench.decode_bytes(d, None) == 2 * 16 * (2 * 8 * 16384 * 128 + 2 * 8 * 128)
+
+
+def test_traffic_figure_is_keyed_to_the_kernel_source():
+    sys.path.insert(0, ROOT)
+    import bench
+    digest = bench.kernel_source_digest()
+    assert len(digest) == 16
+    # a mismatching digest gives no figure rather than a stale one
+    assert bench.committed_traffic("long_bf16_b1h16t16384d128", "0" * 16) is None
+    assert bench.committed_traffic("no_such_workload", digest) is None
