@@ -57,6 +57,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 # includes and its argument struct (the rest of attn_launch.h declares other kernels)
 KERNEL_SOURCES = ["attn_fwd_kernel.hip", "attn_device.h"]
 
+# the forward workloads timed one by one in the `workloads` object (decode workloads are
+# measured by their own kernels)
+FORWARD_WORKLOADS = ["sdpa_f32_b1h8t64d64", "enc_self_bf16_b32h8t256d64_keypad",
+                     "dec_causal_bf16_b16h16t1024d64", "cross_bf16_b16h16q512k1024d64_keypad",
+                     "long_bf16_b1h16t16384d128", "long_causal_bf16_b1h16t16384d128"]
+
 
 def kernel_source_digest() -> str:
     """Short hash of the forward kernel's sources (keys the committed counter data)."""
@@ -347,6 +353,123 @@ def time_mha(torch, tsd, name, steps, warmup):
     }
 
 
+def algorithmic_flops(w, key_lens) -> float:
+    """4*d flops per (query row, allowed key) pair, counting exactly the allowed pairs:
+    sum_b L_b keys per row under key padding, min(i+1, Tk) keys for row i under the causal mask."""
+    import numpy as np
+    Tq, Tk = w.Tq, w.Tk
+    if w.keypad:
+        lens = np.clip(np.asarray(key_lens), 0, Tk).astype(np.float64)
+    else:
+        lens = np.full(w.B, float(Tk))
+    per_b = []
+    for L in lens:
+        if w.causal:
+            i = np.arange(Tq, dtype=np.float64)
+            per_b.append(np.minimum(i + 1, L).sum())
+        else:
+            per_b.append(Tq * L)
+    return 4.0 * w.h * w.d * float(sum(per_b))
+
+
+def time_workloads(torch, tsd, names, min_calls=100, min_seconds=1.0, max_calls=5000, cold_calls=100):
+    """Each forward workload on its own: 20 warm-up calls, then every call timed alone with a pair
+    of HIP events on the launch stream, at least `min_calls` and `min_seconds` of calls (at most
+    `max_calls`); median and minimum per call.  Workloads whose compulsory bytes fit in the
+    256 MiB last-level cache are also timed "cold": a 512 MiB device write between calls.  The
+    oracle is timed beside each one on the host: whole when it is small, else on the seeded
+    256-row subset of every head."""
+    import statistics
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention_fp64
+    from transformer_scaled_dot_03_amd.workloads import WORKLOADS, make_inputs, sample_rows
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    cores = len(os.sched_getaffinity(0))
+    flush = None
+    res = {}
+    for name in names:
+        w = WORKLOADS[name]
+        q, k, v, kl = make_inputs(w, seed=0)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        kld = None if kl is None else kl.to(dev)
+        out = torch.empty((w.B, w.h, w.Tq, w.d), dtype=qd.dtype, device=dev)
+        fn = tsd.attn_fwd if w.dtype == "bf16" else tsd.attn_fwd_f32
+        mask = (tsd.MASK_CAUSAL if w.causal else 0) | (tsd.MASK_KEYPAD if w.keypad else 0)
+        args = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), out.data_ptr(), w.B, w.h, w.Tq, w.Tk,
+                w.d, w.d, w.scale, mask, None if kld is None else kld.data_ptr(), st)
+
+        def call():
+            rc = fn(*args)
+            if rc != tsd.OK:
+                raise RuntimeError(f"attn_fwd failed on {name}: {tsd.attn_status_str(rc)}")
+
+        def timed(n, between=None):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min(n, 200))]
+            ms = []
+            while len(ms) < n:
+                batch = evs[:min(len(evs), n - len(ms))]
+                for e0, e1 in batch:
+                    if between is not None:
+                        between()
+                    e0.record(stream)
+                    call()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                ms.extend(e0.elapsed_time(e1) for e0, e1 in batch)
+            return ms
+
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        probe = statistics.median(timed(20))
+        n = int(min(max(min_calls, min_seconds * 1e3 / max(probe, 1e-6)), max_calls))
+        ms = timed(n)
+        med, mn = statistics.median(ms), min(ms)
+        fl = flops_per_step(w)
+        alg = algorithmic_flops(w, kl)
+        cb = compulsory_bytes(w)
+        r = {"calls": n, "median_ms": round(med, 5), "min_ms": round(mn, 5),
+             "tflops": round(fl / (med * 1e-3) / 1e12, 2),
+             "algorithmic_tflops": round(alg / (med * 1e-3) / 1e12, 2),
+             "hbm_GBs": round(cb / (med * 1e-3) / 1e9, 1)}
+        if cb <= (256 << 20):
+            if flush is None:
+                flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
+            cms = timed(cold_calls, between=lambda: flush.fill_(1.0))
+            r["cold_median_ms"] = round(statistics.median(cms), 5)
+            r["cold_min_ms"] = round(min(cms), 5)
+        del qd, kd, vd, kld, out
+
+        # the oracle beside it, on the same inputs
+        qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+        kln = None if kl is None else kl.numpy()
+        small = fl <= 40e9
+        rows = None if small else sample_rows(w.Tq, 256, seed=0).numpy()
+        with threadpool_limits(limits=cores):
+            t0 = time.perf_counter()
+            attention_fp64(qn, kn, vn, w.scale, causal=w.causal, key_lens=kln, rows=rows)
+            el = time.perf_counter() - t0
+        orc = {"seconds": round(el, 3), "cores": cores,
+               "sample": "whole workload" if small else f"{len(rows)} seeded query rows x {w.B * w.h} heads"}
+        if rows is not None:
+            orc["rows_per_s"] = round(len(rows) * w.B * w.h / el, 1)
+        if w.Tq * w.Tk * w.B * w.h <= 1 << 20:
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                attention_fp64(qn, kn, vn, w.scale, causal=w.causal, key_lens=kln)
+                orc["seconds_1_thread"] = round(time.perf_counter() - t0, 4)
+        r["oracle"] = orc
+        res[name] = r
+    return res
+
+
 def compulsory_bytes(w) -> float:
     es = 2 if w.dtype == "bf16" else 4
     return float(es * w.B * w.h * (2 * w.Tq * w.d + 2 * w.Tk * w.d))
@@ -404,6 +527,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-weights", action="store_true", help="skip the weights-output measurement")
     ap.add_argument("--no-mha", action="store_true", help="skip the multi-head wrapper measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the per-workload forward timings (median / min / cold, oracle beside)")
     ap.add_argument("--decode-workload", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
@@ -507,6 +632,8 @@ def main():
         rec["weights"] = time_weights(torch, tsd, "dec_causal_bf16_b16h16t1024d64", args.steps, args.warmup)
     if not args.no_mha:
         rec["mha"] = time_mha(torch, tsd, "mha_self_bf16_b32t1024dm512h8", args.steps, args.warmup)
+    if not args.no_workloads:
+        rec["workloads"] = time_workloads(torch, tsd, FORWARD_WORKLOADS)
     if not args.no_mfma_probe and w.dtype == "bf16":
         rec["mfma_ceiling"] = mfma_ceiling(torch, dev)
     if not args.no_cpu_baseline:

@@ -38,3 +38,19 @@ def test_traffic_figure_is_keyed_to_the_kernel_source():
     # a mismatching digest gives no figure rather than a stale one
     assert bench.committed_traffic("long_bf16_b1h16t16384d128", "0" * 16) is None
     assert bench.committed_traffic("no_such_workload", digest) is None
+
+
+def test_algorithmic_flops_count_exactly_the_allowed_pairs():
+    sys.path.insert(0, ROOT)
+    import bench
+    from transformer_scaled_dot_03_amd.workloads import MASK_CAUSAL, MASK_KEYPAD, Workload
+    # brute-force pair count on small shapes, every mask combination, Tq != Tk included
+    for Tq, Tk in ((5, 7), (7, 5), (6, 6)):
+        for mask in (0, MASK_CAUSAL, MASK_KEYPAD, MASK_CAUSAL | MASK_KEYPAD):
+            w = Workload("t", 3, 2, Tq, Tk, 4, "bf16", mask, 0.5)
+            lens = [0, 3, Tk + 4]   # clamped to [0, Tk] as the kernels do
+            pairs = 0
+            for b in range(w.B):
+                L = min(max(lens[b], 0), Tk) if w.keypad else Tk
+                pairs += sum(1 for i in range(Tq) for j in range(Tk) if j < L and (not w.causal or j <= i))
+            assert bench.algorithmic_flops(w, lens) == 4.0 * w.h * w.d * pairs
