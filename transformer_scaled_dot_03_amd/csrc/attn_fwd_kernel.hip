@@ -55,10 +55,11 @@ namespace attn {
 //           read from LDS feeds two MFMAs (half the LDS reads per flop), at
 //           the price of ~400 registers (accumulators in AGPRs): one wave per SIMD;
 //   kBN     keys per pipeline step (the K/V tile);
-//   kBuf    K/V tile buffers per tensor (prefetch distance kBuf - 1 tiles);
-//   kPipe   compute the next tile's scores while the current tile's softmax
-//           runs (K staged one tile ahead of V); else scores, softmax and PV
-//           of a tile in sequence, K and V staged together.
+//   kBuf    K/V tile buffers per tensor (2 for the pipelined step);
+//   kPipe   software pipeline: each step interleaves the matrix operations of
+//           one tile with the vector work of another (K staged one tile ahead,
+//           V one tile behind); else scores, softmax and PV of a tile in
+//           sequence, K and V staged together.
 // Measured on MI355X for d = 128 (T = 16384): 8 waves x 1 group x 64 keys x 2
 // buffers is fastest; two row groups (one wave per SIMD) ran ~30% slower and
 // deeper prefetch (3 or 4 buffers) did not help.
@@ -83,7 +84,6 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   constexpr int BN = Bf16Shape<D>::kBN;      // keys per tile
   constexpr int NBUF = Bf16Shape<D>::kBuf;   // tile buffers per tensor
   constexpr bool PIPE = Bf16Shape<D>::kPipe;
-  constexpr int UNR = NBUF % 2 == 0 ? NBUF : 2 * NBUF;   // steps per loop trip
   constexpr int NH = BN / 32;                // 32-key slices per tile
   constexpr int BM = 32 * RG * WAVES;        // query rows per work-group
   constexpr int ROWB = D * 2;                // bytes per K / V row
@@ -337,68 +337,162 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   };
 
   if constexpr (PIPE) {
-    // Software pipeline, one BN-key tile per step: the matrix cores compute
-    // the scores of tile j+1 while the vector ALUs turn the scores of tile j
-    // into probabilities, then O^T += V^T P^T for tile j.  K is therefore
-    // staged one tile ahead of V: step j reads K(j+1) and V(j) and prefetches
-    // K(j+NBUF) and V(j+NBUF-1).
+    // Step j: O^T += V^T P(j-1)^T on the matrix cores interleaved with the row
+    // maxima of tile j on the vector ALUs; the (rare) rescale; then S(j+1) =
+    // K(j+1) Q^T on the matrix cores interleaved with the exponentials of
+    // tile j.  Step j reads V(j-1) and K(j+1) and loads K(j+2) and V(j).
+    // A wave issues in order and an MFMA waits for the matrix pipe, so
+    // without the pinned interleave the compiler's order (all MFMAs of a
+    // block, then all vector work) leaves one unit idle while the other runs.
+    static_assert(NBUF == 2, "the pipelined step uses plain double buffering");
     f32x16 s2[2][RG][NH];
-    // MASKED: the tile may hold masked keys for some row of the work-group
-    // (the interior steps carry no mask code, so the scores of the next tile
-    // and this tile's row maxima share one basic block)
-    auto step = [&](int it, auto U, auto MASKED) {
-      constexpr int u = decltype(U)::value;   // it % UNR (buffer index and score parity)
-      f32x16 (&sc)[RG][NH] = s2[u & 1];
-      f32x16 (&sn)[RG][NH] = s2[(u + 1) & 1];
-      const int j0 = it * BN;
-      if (it + NBUF < ntiles) load_k(j0 + NBUF * BN, kbuf(std::integral_constant<int, u>{}));
-      if (it + NBUF - 1 < ntiles)
-        load_v(j0 + (NBUF - 1) * BN, vbuf(std::integral_constant<int, u + NBUF - 1>{}));
-      if (it < ntw) {
-        // scores of the next tile (unused past the wave's last tile): the
-        // matrix cores work on them while the vector ALUs take this tile's max
-        scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
-        mask_and_rescale(j0, sc, MASKED);
-        bf16x8 pk[RG][NH][2];
-        probabilities(sc, pk);
-        pv(vbuf(std::integral_constant<int, u>{}), pk);
-      }
-      // The next step reads K(it+2) and V(it+1), loaded by step it+2-NBUF:
-      // only the loads of the NBUF-2 most recent steps may stay in flight.
-      int batches = 0;
+    bf16x8 pk[RG][NH][2];
+    float m_tile[RG];
+    auto row_max = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) -> bool {
+      if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
 #pragma unroll
-      for (int k = 0; k < NBUF - 2; ++k) {
-        const int sk = it - k;
-        if (sk >= 0) batches += (sk + NBUF < ntiles) + (sk + NBUF - 1 < ntiles);
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+              bool ok = key < kend;
+              if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
+              sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
+            }
       }
-      static_for<0, 2 * (NBUF - 2) + 1>([&](auto N) {
-        if (batches == N) pipeline_barrier<N * NLD>();
+      bool grow = false;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        float mx[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mx[k] = sc[r][k / 2][8 * (k % 2)];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx[(2 * hh + e / 8) % 4] = fmaxf(mx[(2 * hh + e / 8) % 4], sc[r][hh][e]);
+        m_tile[r] = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * cs;
+        grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
+      }
+      return grow;
+    };
+    auto rescale = [&]() {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const float m_new = fmaxf(m_run[r], m_tile[r]);
+        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);
+        m_run[r] = m_new;
+        base[r] = b_new;
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
+      }
+    };
+    auto probs = [&](const f32x16 (&sc)[RG][NH]) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            f32x8 e8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
+            pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
+              l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
+            }
+          }
+    };
+    constexpr int NPV = NH * 2 * NO * RG;   // P V^T operations, 2 LDS reads each
+    constexpr int NS = NH * DT * RG;        // score operations, 1 LDS read each
+    // block A order: 8 reads, then per operation: 1 MFMA, 2 VALU, 2 reads
+    auto pin_a = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+      static_for<0, NPV>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 2);
+        if constexpr (i + 4 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
       });
     };
+    // block C order: 4 reads, then per operation: 1 MFMA, 7 VALU, 1 read
+    auto pin_c = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
+      static_for<0, NS>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 3);
+        if constexpr (i + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+      });
+    };
+    // the probabilities and row sums stay in the step that computes them (the
+    // compiler would otherwise sink them past the barrier into the next step)
+    auto pin_p = [&]() {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) asm volatile("" ::"v"(pk[r][hh][m]));
+        asm volatile("" ::"v"(l_run[r]));
+      }
+    };
+    // it: step index; U: it % 2 (buffer parity)
+    auto step = [&](int it, auto U, auto MASKED) {
+      constexpr int u = decltype(U)::value;
+      f32x16 (&sc)[RG][NH] = s2[u];
+      f32x16 (&sn)[RG][NH] = s2[u ^ 1];
+      const int j0 = it * BN;
+      if (it + 2 < ntiles) load_k(j0 + 2 * BN, kbuf(std::integral_constant<int, u>{}));
+      if (it < ntiles) load_v(j0, vbuf(std::integral_constant<int, u>{}));
+      if constexpr (!decltype(MASKED)::value) {
+        pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
+        const bool grow = row_max(j0, sc, MASKED);
+        pin_a();
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
+        scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+        probs(sc);
+        pin_c();
+        pin_p();
+      } else {
+        if (it >= 1 && it - 1 < ntw) pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
+        if (it < ntw) {
+          const bool grow = row_max(j0, sc, MASKED);
+          if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
+          if (it + 1 < ntw) scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+          probs(sc);
+          pin_p();
+        }
+      }
+      pipeline_barrier<0>();
+    };
 
-    // prologue: K(0 .. NBUF-1) and V(0 .. NBUF-2), then the scores of tile 0
-    static_for<0, NBUF>([&](auto I) {
-      if (I < ntiles) load_k(I * BN, kbuf(I));
-    });
-    static_for<0, NBUF - 1>([&](auto I) {
-      if (I < ntiles) load_v(I * BN, vbuf(I));
-    });
+    // prologue: K(0), K(1); the scores of tile 0; K(0) consumed before step 0 reloads its buffer
+    if (ntiles > 0) load_k(0, kb0);
+    if (ntiles > 1) load_k(BN, kb1);
     pipeline_barrier<0>();
     if (ntw > 0) scores(kb0, s2[0]);
-    pipeline_barrier<0>();             // K(0) consumed: its buffer takes K(NBUF)
-    // tiles [0, nint) hold no masked key for any row of the work-group: keys
-    // below kend and (causal) below its first row; a multiple of UNR, so the
-    // masked loop starts on buffer 0
+    pipeline_barrier<0>();
+    // tiles [0, nint) hold no masked key for any row of the work-group
     int nint = kend / BN;
     if (CAUSAL) nint = min(nint, (q0 + 1) / BN);
-    nint = min(nint, ntiles) / UNR * UNR;
-    for (int it0 = 0; it0 < nint; it0 += UNR) {
-      static_for<0, UNR>([&](auto U) { step(it0 + U, U, std::false_type{}); });
+    nint = min(nint, ntiles);
+    // steps 0 .. ntiles; step 0 (no P V^T yet) and steps >= nint take the general path
+    step(0, std::integral_constant<int, 0>{}, std::true_type{});
+    int it0 = 1;
+    for (; it0 + 1 < nint; it0 += 2) {
+      step(it0, std::integral_constant<int, 1>{}, std::false_type{});
+      step(it0 + 1, std::integral_constant<int, 0>{}, std::false_type{});
     }
-    for (int it0 = nint; it0 < ntiles; it0 += UNR) {
-      static_for<0, UNR>([&](auto U) {
-        if (it0 + U < ntiles) step(it0 + U, U, std::true_type{});
-      });
+    for (; it0 <= ntiles; it0 += 2) {
+      step(it0, std::integral_constant<int, 1>{}, std::true_type{});
+      if (it0 + 1 <= ntiles) step(it0 + 1, std::integral_constant<int, 0>{}, std::true_type{});
     }
   } else {
     // One tile per step in sequence (scores, softmax, PV); K(j+1) and V(j+1)
