@@ -395,17 +395,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
 
   if (ntiles > 0) load_tile(first * kBT, qb0, gb0, rb0);
   pipeline_barrier<0>();
-  for (int it0 = 0; it0 < ntiles; it0 += 2) {
-    static_for<0, 2>([&](auto U) __attribute__((always_inline)) {
-      constexpr int u = decltype(U)::value;
-      const int it = it0 + u;
-      if (it < ntiles) {
-        if (it + 1 < ntiles) load_tile((first + it + 1) * kBT, u ? qb0 : qb1, u ? gb0 : gb1, u ? rb0 : rb1);
-        step(first + it, u ? qb1 : qb0, u ? gb1 : gb0, u ? rb1 : rb0);
-        pipeline_barrier<0>();
-      }
-    });
+  // pairs of tiles with no condition around the accumulating steps (a
+  // conditional step makes the compiler shuttle dK and dV between register
+  // files at every trip), then the odd last tile
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    load_tile((first + it + 1) * kBT, qb1, gb1, rb1);
+    step(first + it, qb0, gb0, rb0);
+    pipeline_barrier<0>();
+    if (it + 2 < ntiles) load_tile((first + it + 2) * kBT, qb0, gb0, rb0);
+    step(first + it + 1, qb1, gb1, rb1);
+    pipeline_barrier<0>();
   }
+  if (it < ntiles) step(first + it, qb0, gb0, rb0);
   if (key < Tk) {
     store_row<D>(static_cast<__bf16*>(p.dk) + koff, key, g, p.scale, adk);
     store_row<D>(static_cast<__bf16*>(p.dv) + koff, key, g, 1.0f, adv);
