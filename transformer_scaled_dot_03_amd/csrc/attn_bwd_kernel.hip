@@ -532,6 +532,18 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
     }
   };
 
+  // tiles past the causal / padding limit of the work-group are zeros, written
+  // row-wise (16 lanes cover one row's 64 keys).  Without the causal mask (zero
+  // tiles from key padding) one goes out after each computed tile, so the pure
+  // writes overlap the computing tiles (+12% on the cross-attention workload);
+  // with it the longest-first order already puts the zero-heavy groups last
+  const f32x4 z4 = f32x4{};
+  int zt = ntiles;
+  auto zero_tile = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) store4((lane >> 4) + 4 * i, zt * kBT + 4 * (lane & 15), z4);
+    ++zt;
+  };
   if (ntiles > 0) load_k(0, kb0);
   pipeline_barrier<0>();
   for (int it0 = 0; it0 < ntiles; it0 += 2) {
@@ -541,16 +553,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
       if (it < ntiles) {
         if (it + 1 < ntiles) load_k((it + 1) * kBT, u ? kb0 : kb1);
         step(it, u ? kb1 : kb0);
+        if (!CAUSAL && zt < nall) zero_tile();
         pipeline_barrier<0>();
       }
     });
   }
-  // tiles past the causal / padding limit of the work-group: zeros, written
-  // row-wise (16 lanes cover one row's 64 keys)
-  const f32x4 z4 = f32x4{};
-  for (int it = ntiles; it < nall; ++it)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) store4((lane >> 4) + 4 * i, it * kBT + 4 * (lane & 15), z4);
+  while (zt < nall) zero_tile();
 }
 
 // ---------------------------------------------------------------------------
