@@ -14,8 +14,10 @@
 //   * attn_bwd_dq_kernel: one work-group per 128 query rows; writes D_i and
 //     lse_i log2(e) to the caller's workspace, then streams K/V tiles of 64
 //     keys and accumulates dQ in registers;
-//   * attn_bwd_dkdv_kernel: one work-group per 128 keys; streams Q/dO tiles of
-//     64 rows (with their D and lse log2(e)) and accumulates dK, dV in registers.
+//   * attn_bwd_dkdv_kernel: one work-group per 128 keys (d = 64) or 256 keys
+//     (d = 128: 8 waves, V's rows held in LDS so two waves fit on a SIMD);
+//     streams Q/dO tiles of 64 rows (with their D and lse log2(e)) and
+//     accumulates dK, dV in registers.
 // Matrix-core mapping as in the forward (v_mfma_f32_32x32x16_bf16, lane l,
 // g = l / 32, c = l % 32): products whose output rows are the lane's own
 // row/key take the streamed operand from LDS as 16-byte fragments read in
@@ -49,12 +51,12 @@ struct BwdTile {
 
 // direct-to-LDS source offsets of this lane for a row-major 64-row tile,
 // stored with the dual swizzle
-template <int D>
-__device__ __forceinline__ void tile_src_offsets(int w, int lane, uint32_t (&src)[BwdTile<D>::NLD]) {
+template <int D, int W = kBwdWaves>
+__device__ __forceinline__ void tile_src_offsets(int w, int lane, uint32_t (&src)[BwdTile<D>::TILEB / 1024 / W]) {
   constexpr int ROWB = BwdTile<D>::ROWB;
 #pragma unroll
-  for (int u = 0; u < BwdTile<D>::NLD; ++u) {
-    const int pos = (kBwdWaves * u + w) * 1024 + 16 * lane;
+  for (int u = 0; u < BwdTile<D>::TILEB / 1024 / W; ++u) {
+    const int pos = (W * u + w) * 1024 + 16 * lane;
     const int r = pos / ROWB, pc = (pos % ROWB) / 16;
     src[u] = r * ROWB + 16 * (pc ^ dual_swz<D>(r));
   }
@@ -86,6 +88,14 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&rd)[BwdTile<D>::NO][2
       rd[i][e] = r * BwdTile<D>::ROWB + 16 * (lc ^ dual_swz<D>(r)) + 8 * ((sl >> 1) & 1);
     }
   }
+}
+
+// base ^ imm computed where it is used: an asm the compiler cannot hoist, so a
+// set of per-step LDS offsets costs one register instead of one each
+__device__ __forceinline__ int xor_at_use(int base, int imm) {
+  int r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(imm), "v"(base));
+  return r;
 }
 
 // A operand (8 consecutive rows of the transposed tile) from two transposed reads
@@ -269,11 +279,24 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 // ---------------------------------------------------------------------------
 // dK / dV kernel
 // ---------------------------------------------------------------------------
+// dK/dV work-group shape: d = 128 runs 8 waves (two per SIMD, 256 keys) with
+// V's rows in LDS, so a wave holds only its K row and the accumulators; d = 64
+// fits 4 waves with K and V in registers
+template <int D>
+struct DkdvShape {
+  static constexpr int kWaves = D == 128 ? 8 : kBwdWaves;
+  static constexpr bool kVInLds = D == 128;
+};
+
 template <int D, bool CAUSAL, bool KEYPAD>
-__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using TG = BwdTile<D>;
-  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT, NO = TG::NO;
-  constexpr int BK = 32 * kBwdWaves;
+  constexpr int W = DkdvShape<D>::kWaves;
+  constexpr bool VLDS = DkdvShape<D>::kVInLds;
+  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, DT = TG::DT, NO = TG::NO;
+  constexpr int NLD = TILEB / 1024 / W;
+  constexpr int BK = 32 * W;
+  static_assert(NLD >= 1, "tile shape");
 
   __shared__ __attribute__((aligned(1024))) char qb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char qb1[TILEB];
@@ -282,6 +305,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   // per tile: lse * log2(e) of its 64 rows in [0, 64), D in [64, 128)
   __shared__ __attribute__((aligned(256))) float rb0[128];
   __shared__ __attribute__((aligned(256))) float rb1[128];
+  // V rows of the work-group's keys: chunk k of row r at k ^ (r % 16)
+  __shared__ __attribute__((aligned(1024))) char vrows[VLDS ? BK * ROWB : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,20 +329,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   const float* Lg = p.delta + (int64_t)p.B * p.H * Tq + (int64_t)bh * Tq;       // lse * log2(e)
 
   // this lane's key row: K negated for a negative scale (S = scale Q K^T), and V
-  bf16x8 kf[DT], vf[DT];
+  bf16x8 kf[DT], vf[VLDS ? 1 : DT];
   load_row<D>(static_cast<const __bf16*>(p.k) + koff, key, kend, g, p.neg != 0, kf);
-  load_row<D>(static_cast<const __bf16*>(p.v) + koff, key, kend, g, false, vf);
+  int vbase = 0;
+  if constexpr (VLDS) {
+    // the work-group's V rows into LDS once (rows at or past kend read as zero)
+    const __bf16* Vb = static_cast<const __bf16*>(p.v) + koff + (int64_t)k0 * D;
+    const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vb, (uint32_t)max(min(kend - k0, BK), 0) * ROWB);
+#pragma unroll
+    for (int u = 0; u < BK * ROWB / 1024 / W; ++u) {
+      const int pos = (W * u + w) * 1024 + 16 * lane;
+      const int r = pos / ROWB, sc = (pos % ROWB) / 16;
+      lds_dma16(vr, vrows + (W * u + w) * 1024, r * ROWB + 16 * (sc ^ (r & 15)));
+    }
+    // chunk 2t + g of row 32w + c sits at (2t + g) ^ (c % 16): one base XOR 32 t
+    vbase = (32 * w + c) * ROWB + 16 * (g ^ (c & 1)) + 32 * ((c & 15) >> 1);
+  } else {
+    load_row<D>(static_cast<const __bf16*>(p.v) + koff, key, kend, g, false, vf);
+  }
 
   uint32_t src[NLD];
-  tile_src_offsets<D>(w, lane, src);
+  tile_src_offsets<D, W>(w, lane, src);
   auto load_tile = [&](int r0, char* qt, char* gt, float* rt) __attribute__((always_inline)) {
     const uint32_t bytes = (uint32_t)(Tq - r0) * ROWB;
     const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(Qg + (int64_t)r0 * D, bytes);
     const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(Gg + (int64_t)r0 * D, bytes);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      lds_dma16(qr, qt + (kBwdWaves * u + w) * 1024, src[u]);
-      lds_dma16(gr, gt + (kBwdWaves * u + w) * 1024, src[u]);
+      lds_dma16(qr, qt + (W * u + w) * 1024, src[u]);
+      lds_dma16(gr, gt + (W * u + w) * 1024, src[u]);
     }
     // lse * log2(e) (wave 0) and D (wave 1) of rows r0 .. r0 + 63; rows at or past Tq read as 0
     if (w < 2) {
@@ -329,6 +369,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
   frag_offsets<D>(c, g, fr);
   int trd[NO][2];
   tr_offsets<D>(lane, trd);
+  // with d = 128 the step offsets are base ^ 32 t (fragment reads, V rows) and
+  // base ^ 32 i (transposed reads): keep the bases only (two waves share a SIMD)
+  const int fbase = fr[0], tb0 = trd[0][0], tb1 = trd[0][1];
+  auto frag_at = [&](int t) __attribute__((always_inline)) { return VLDS ? xor_at_use(fbase, 32 * t) : fr[t]; };
+  auto tr_at = [&](int i, int e) __attribute__((always_inline)) {
+    return VLDS ? xor_at_use(e ? tb1 : tb0, 32 * i) : trd[i][e];
+  };
 
   f32x16 adk[NO], adv[NO];
 #pragma unroll
@@ -343,10 +390,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + 32 * hh * ROWB + fr[t]);
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + 32 * hh * ROWB + frag_at(t));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], s, 0, 0, 0);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt + 32 * hh * ROWB + fr[t]);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[t], dp, 0, 0, 0);
+        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt + 32 * hh * ROWB + frag_at(t));
+        bf16x8 vt;
+        if constexpr (VLDS) vt = *reinterpret_cast<const bf16x8*>(vrows + xor_at_use(vbase, 32 * t));
+        else vt = vf[t];
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vt, dp, 0, 0, 0);
       }
       // register e: row r0 + 32hh + 16(e/8) + 8g + e%8 for this lane's key
 #pragma unroll
@@ -384,10 +434,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         const char* qtm = qt + (32 * hh + 16 * m) * ROWB;
 #pragma unroll
         for (int i = 0; i < NO; ++i) {
-          adv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(gtm + trd[i][0], gtm + trd[i][1]), pb,
-                                                           adv[i], 0, 0, 0);
-          adk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qtm + trd[i][0], qtm + trd[i][1]), dsb,
-                                                           adk[i], 0, 0, 0);
+          const int o0 = tr_at(i, 0), o1 = tr_at(i, 1);
+          adv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(gtm + o0, gtm + o1), pb, adv[i], 0, 0, 0);
+          adk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qtm + o0, qtm + o1), dsb, adk[i], 0, 0, 0);
         }
       }
     }
@@ -575,7 +624,7 @@ static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t stream) {
   }
   if (prm.Tk > 0)
     return hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<D, C, P>),
-                           dim3(prm.B * prm.H * prm.n_ktiles), dim3(kBwdThreads), args, 0, stream);
+                           dim3(prm.B * prm.H * prm.n_ktiles), dim3(64 * DkdvShape<D>::kWaves), args, 0, stream);
   return hipSuccess;
 }
 
@@ -607,7 +656,7 @@ hipError_t launch_weights(const WtsParams& prm, int d, bool causal, bool keypad,
 }
 
 int bwd_rows_per_block(int) { return 32 * kBwdWaves; }
-int bwd_keys_per_block(int) { return 32 * kBwdWaves; }
+int bwd_keys_per_block(int d) { return d == 128 ? 32 * DkdvShape<128>::kWaves : 32 * DkdvShape<64>::kWaves; }
 
 hipError_t launch_bwd(const BwdParams& prm, int d, bool causal, bool keypad, hipStream_t stream) {
   return d == 64 ? launch_bwd_mask<64>(prm, causal, keypad, stream)
