@@ -11,9 +11,9 @@
 // training of every weight matrix).
 //
 // Two kernels, no atomics and no scratch beyond the caller's delta array:
-//   * attn_bwd_dq_kernel: one work-group per 128 query rows; writes D_i and
-//     lse_i log2(e) to the caller's workspace, then streams K/V tiles of 64
-//     keys and accumulates dQ in registers;
+//   * attn_bwd_dq_kernel: one work-group per 128 query rows (d = 64) or 256
+//     (d = 128); writes D_i and lse_i log2(e) to the caller's workspace, then
+//     streams K/V tiles of 64 keys and accumulates dQ in registers;
 //   * attn_bwd_dkdv_kernel: one work-group per 128 keys (d = 64) or 256 keys
 //     (d = 128: 8 waves, V's rows held in LDS so two waves fit on a SIMD);
 //     streams Q/dO tiles of 64 rows (with their D and lse log2(e)) and
@@ -138,11 +138,20 @@ __device__ __forceinline__ void store_row(__bf16* base, int row, int g, float mu
 // ---------------------------------------------------------------------------
 // dQ (and D) kernel
 // ---------------------------------------------------------------------------
+// dQ work-group shape: d = 128 runs 8 waves (256 rows, two waves per SIMD), so
+// each K/V tile staged in LDS serves twice as many rows; d = 64 runs 4
+template <int D>
+struct DqShape {
+  static constexpr int kWaves = D == 128 ? 8 : kBwdWaves;
+};
+
 template <int D, bool CAUSAL, bool KEYPAD>
-__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(64 * DqShape<D>::kWaves, 8 / DqShape<D>::kWaves) void attn_bwd_dq_kernel(BwdParams p) {
   using TG = BwdTile<D>;
-  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, NLD = TG::NLD, DT = TG::DT, NO = TG::NO;
-  constexpr int BM = 32 * kBwdWaves;
+  constexpr int W = DqShape<D>::kWaves;
+  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, DT = TG::DT, NO = TG::NO;
+  constexpr int NLD = TILEB / 1024 / W;
+  constexpr int BM = 32 * W;
   constexpr float kNegInf = -__builtin_inff(), kPosInf = __builtin_inff();
 
   __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
@@ -196,15 +205,15 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
   }
 
   uint32_t src[NLD];
-  tile_src_offsets<D>(w, lane, src);
+  tile_src_offsets<D, W>(w, lane, src);
   auto load_kv = [&](int j0, char* kt, char* vt) __attribute__((always_inline)) {
     const uint32_t bytes = (uint32_t)(kend - j0) * ROWB;
     const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(Kg + (int64_t)j0 * D, bytes);
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vg + (int64_t)j0 * D, bytes);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      lds_dma16(kr, kt + (kBwdWaves * u + w) * 1024, src[u]);
-      lds_dma16(vr, vt + (kBwdWaves * u + w) * 1024, src[u]);
+      lds_dma16(kr, kt + (W * u + w) * 1024, src[u]);
+      lds_dma16(vr, vt + (W * u + w) * 1024, src[u]);
     }
   };
   int fr[DT];
@@ -619,7 +628,8 @@ static hipError_t launch_bwd_d(const BwdParams& prm, hipStream_t stream) {
   void* args[] = {&local};
   if (prm.Tq > 0) {
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dq_kernel<D, C, P>),
-                                         dim3(prm.B * prm.H * prm.n_qtiles), dim3(kBwdThreads), args, 0, stream);
+                                         dim3(prm.B * prm.H * prm.n_qtiles), dim3(64 * DqShape<D>::kWaves), args,
+                                         0, stream);
     if (e != hipSuccess) return e;
   }
   if (prm.Tk > 0)
@@ -655,7 +665,7 @@ hipError_t launch_weights(const WtsParams& prm, int d, bool causal, bool keypad,
                  : launch_weights_mask<128>(prm, causal, keypad, stream);
 }
 
-int bwd_rows_per_block(int) { return 32 * kBwdWaves; }
+int bwd_rows_per_block(int d) { return d == 128 ? 32 * DqShape<128>::kWaves : 32 * DqShape<64>::kWaves; }
 int bwd_keys_per_block(int d) { return d == 128 ? 32 * DkdvShape<128>::kWaves : 32 * DkdvShape<64>::kWaves; }
 
 hipError_t launch_bwd(const BwdParams& prm, int d, bool causal, bool keypad, hipStream_t stream) {
