@@ -64,16 +64,25 @@ FORWARD_WORKLOADS = ["sdpa_f32_b1h8t64d64", "enc_self_bf16_b32h8t256d64_keypad",
                      "long_bf16_b1h16t16384d128", "long_causal_bf16_b1h16t16384d128"]
 
 
+def code_only(src: bytes) -> bytes:
+    """C++ source with comments removed and whitespace collapsed: edits to comments
+    leave the compiled kernel, and so the digest, unchanged."""
+    text = src.decode()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split()).encode()
+
+
 def kernel_source_digest() -> str:
-    """Short hash of the forward kernel's sources (keys the committed counter data)."""
+    """Short hash of the forward kernel's code (keys the committed counter data)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "csrc")
     for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+            h.update(name.encode() + b"\0" + code_only(f.read()))
     launch = open(os.path.join(csrc, "attn_launch.h"), "rb").read()
     m = re.search(rb"struct Params \{.*?\};", launch, flags=re.S)
-    h.update(b"Params\0" + (m.group(0) if m else launch))
+    h.update(b"Params\0" + code_only(m.group(0) if m else launch))
     return h.hexdigest()[:16]
 
 

@@ -54,3 +54,13 @@ def test_algorithmic_flops_count_exactly_the_allowed_pairs():
                 L = min(max(lens[b], 0), Tk) if w.keypad else Tk
                 pairs += sum(1 for i in range(Tq) for j in range(Tk) if j < L and (not w.causal or j <= i))
             assert bench.algorithmic_flops(w, lens) == 4.0 * w.h * w.d * pairs
+
+
+def test_digest_ignores_comments_but_not_code():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = b"int f(int x) {  // doubles\n  return 2 * x; /* no\n overflow check */ }\n"
+    b = b"int f(int x) {\n\n  return 2 * x;   }  // reworded note\n"
+    c = b"int f(int x) { return 3 * x; }\n"
+    assert bench.code_only(a) == bench.code_only(b)
+    assert bench.code_only(a) != bench.code_only(c)

@@ -5,10 +5,11 @@
 //   "The idea: every word queries every word"; notebook chapter, sections
 //   "Multi-Head Self-Attention" and "Masked Attention in the Decoder").
 //
-// One work-group (4 waves, 256 threads) owns BM = 128 query rows of one
-// (b, head); wave w owns rows [32w, 32w + 32).  The key/value sequence is
-// streamed in tiles of BN keys through LDS (double-buffered: the global loads
-// of tile t+1 are in flight while tile t is computed).  The softmax is the
+// One work-group owns 32 query rows per wave of one (b, head) (d = 128: 8
+// waves, 256 rows; d = 64: 4 waves, 128 rows); wave w owns rows [32w, 32w + 32).
+// The key/value sequence is streamed in tiles of 64 keys through LDS by
+// direct-to-LDS buffer loads (double-buffered: the loads of the next tiles are
+// in flight while the current ones are computed).  The softmax is the
 // running (online) form: per row a running maximum m and sum l, with the
 // output accumulator rescaled by exp2(m_old - m_new) whenever m grows
 // (Milakov & Gimelshein 2018, "Online normalizer calculation for softmax";
@@ -27,8 +28,13 @@
 //     consecutive keys 16m + 8g + (0..7).  Those 8 probabilities are exactly
 //     the B operand of O^T = V^T P^T for keys 16m .. 16m+15: no data movement
 //     between the two products.
-//   * V is stored transposed in LDS (Vt[dv][key]) while staging, so the A
-//     operand of the second product is one 16-byte LDS read per lane.
+//   * V stays row-major in LDS; the A operand of the second product (8 keys
+//     of one output column per lane) comes from two transposing LDS reads
+//     (ds_read_b64_tr_b16).
+//   * Each step interleaves the matrix operations of one tile with the vector
+//     work of another (P V of the previous tile with this tile's row maxima,
+//     then the next tile's scores with this tile's exponentials), in a pinned
+//     instruction order.
 //   * The output accumulator O^T holds, in lane l, row c and d/2 contiguous
 //     output columns (dv permuted by tau), so the epilogue writes d bytes of
 //     contiguous bf16 per lane.
