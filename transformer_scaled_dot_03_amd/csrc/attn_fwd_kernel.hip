@@ -60,26 +60,19 @@ namespace attn {
 //   kRG     groups of 32 query rows per wave: with 2, every K and V^T fragment
 //           read from LDS feeds two MFMAs (half the LDS reads per flop), at
 //           the price of ~400 registers (accumulators in AGPRs): one wave per SIMD;
-//   kBN     keys per pipeline step (the K/V tile);
-//   kBuf    K/V tile buffers per tensor (2 for the pipelined step);
-//   kPipe   software pipeline: each step interleaves the matrix operations of
-//           one tile with the vector work of another (K staged one tile ahead,
-//           V one tile behind); else scores, softmax and PV of a tile in
-//           sequence, K and V staged together.
-// Measured on MI355X for d = 128 (T = 16384): 8 waves x 1 group x 64 keys x 2
-// buffers is fastest; two row groups (one wave per SIMD) ran ~30% slower and
-// deeper prefetch (3 or 4 buffers) did not help.
+//   kBN     keys per pipeline step (the K/V tile; K and V double-buffered).
+// Measured on MI355X for d = 128 (T = 16384): 8 waves x 1 group x 64 keys is
+// fastest; two row groups (one wave per SIMD) ran ~30% slower and deeper
+// prefetch (3 or 4 buffers) did not help.
 template <int D>
 struct Bf16Shape;
 template <>
 struct Bf16Shape<64> {
-  static constexpr int kWaves = 4, kRG = 1, kBN = 64, kBuf = 2;
-  static constexpr bool kPipe = true;
+  static constexpr int kWaves = 4, kRG = 1, kBN = 64;
 };
 template <>
 struct Bf16Shape<128> {
-  static constexpr int kWaves = 8, kRG = 1, kBN = 64, kBuf = 2;
-  static constexpr bool kPipe = true;
+  static constexpr int kWaves = 8, kRG = 1, kBN = 64;
 };
 
 template <int D, bool CAUSAL, bool KEYPAD>
@@ -88,8 +81,6 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   constexpr int WAVES = Bf16Shape<D>::kWaves;
   constexpr int RG = Bf16Shape<D>::kRG;      // 32-row groups per wave
   constexpr int BN = Bf16Shape<D>::kBN;      // keys per tile
-  constexpr int NBUF = Bf16Shape<D>::kBuf;   // tile buffers per tensor
-  constexpr bool PIPE = Bf16Shape<D>::kPipe;
   constexpr int NH = BN / 32;                // 32-key slices per tile
   constexpr int BM = 32 * RG * WAVES;        // query rows per work-group
   constexpr int ROWB = D * 2;                // bytes per K / V row
@@ -99,35 +90,23 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
   constexpr int NO = D / 32;                 // 32-column tiles of the output
   static_assert(RG == 1 || RG == 2, "row groups");
   static_assert(BN == 32 || BN == 64 || BN == 128, "tile keys");
-  static_assert(PIPE || NBUF == 2, "the sequential step uses plain double buffering");
   static_assert(NLD >= 1 && TILEB % (1024 * WAVES) == 0, "tile shape");
-  static_assert(NBUF >= 2 && NBUF <= 4, "buffers");
   constexpr float kNegInf = -__builtin_inff();
 
-  // NBUF buffers per tensor, each its own array: the compiler can then see
-  // that direct-to-LDS loads into one buffer never alias reads of another,
+  // two buffers per tensor, each its own array: the compiler can then see
+  // that direct-to-LDS loads into one buffer never alias reads of the other,
   // and does not wait for the prefetch before reading the current tile
   __shared__ __attribute__((aligned(1024))) char kb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char kb1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char kb2[NBUF > 2 ? TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) char kb3[NBUF > 3 ? TILEB : 16];
   __shared__ __attribute__((aligned(1024))) char vb0[TILEB];
   __shared__ __attribute__((aligned(1024))) char vb1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char vb2[NBUF > 2 ? TILEB : 16];
-  __shared__ __attribute__((aligned(1024))) char vb3[NBUF > 3 ? TILEB : 16];
   auto kbuf = [&](auto I) -> char* {
-    constexpr int i = decltype(I)::value % NBUF;
-    if constexpr (i == 0) return kb0;
-    else if constexpr (i == 1) return kb1;
-    else if constexpr (i == 2) return kb2;
-    else return kb3;
+    if constexpr (decltype(I)::value % 2 == 0) return kb0;
+    else return kb1;
   };
   auto vbuf = [&](auto I) -> char* {
-    constexpr int i = decltype(I)::value % NBUF;
-    if constexpr (i == 0) return vb0;
-    else if constexpr (i == 1) return vb1;
-    else if constexpr (i == 2) return vb2;
-    else return vb3;
+    if constexpr (decltype(I)::value % 2 == 0) return vb0;
+    else return vb1;
   };
 
   const int tid = threadIdx.x;
@@ -252,77 +231,6 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     }
   };
 
-  // Software pipeline, one BN-key tile per step: the matrix cores compute the
-  // scores of tile j+1 while the vector ALUs turn the scores of tile j into
-  // probabilities, then O^T += V^T P^T for tile j.  K is therefore staged one
-  // tile ahead of V: step j reads K(j+1) and V(j) and prefetches
-  // K(j+NBUF) and V(j+NBUF-1).
-  // Masked scores (edge tiles only; the test is wave uniform) become -inf and,
-  // since cs > 0, exp2 gives them exactly zero weight.
-  // mask (edge tiles only; the test is wave uniform), running max with lazy
-  // rescale; masked scores become -inf and, since cs > 0, exp2 gives them
-  // exactly zero weight
-  auto mask_and_rescale = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) {
-    if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r)
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-            bool ok = key < kend;
-            if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
-            sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
-          }
-    }
-    float m_tile[RG];
-    bool grow = false;
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      float mx = sc[r][0][0];
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[r][hh][e]);
-      m_tile[r] = pair_max(mx) * cs;                 // -inf if the row has no key here
-      grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
-    }
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const float m_new = fmaxf(m_run[r], m_tile[r]);
-        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);   // 0 when m_run = -inf
-        m_run[r] = m_new;
-        base[r] = b_new;
-        l_run[r] *= alpha;
-#pragma unroll
-        for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
-      }
-    }
-  };
-  // probabilities rounded to bf16 (P operand) and their row sum
-  auto probabilities = [&](const f32x16 (&sc)[RG][NH], bf16x8 (&pk)[RG][NH][2]) {
-#pragma unroll
-    for (int r = 0; r < RG; ++r)
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          f32x8 e8;
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
-          pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
-          // row sum of the rounded probabilities actually used in O^T += V^T P^T
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
-            l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
-          }
-        }
-  };
   // O^T += V^T P^T over one V tile
   auto pv = [&](const char* v_cur, const bf16x8 (&pk)[RG][NH][2]) {
 #pragma unroll
@@ -342,7 +250,7 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
         }
   };
 
-  if constexpr (PIPE) {
+  {
     // Step j: O^T += V^T P(j-1)^T on the matrix cores interleaved with the row
     // maxima of tile j on the vector ALUs; the (rare) rescale; then S(j+1) =
     // K(j+1) Q^T on the matrix cores interleaved with the exponentials of
@@ -350,7 +258,6 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     // A wave issues in order and an MFMA waits for the matrix pipe, so
     // without the pinned interleave the compiler's order (all MFMAs of a
     // block, then all vector work) leaves one unit idle while the other runs.
-    static_assert(NBUF == 2, "the pipelined step uses plain double buffering");
     f32x16 s2[2][RG][NH];
     bf16x8 pk[RG][NH][2];
     float m_tile[RG];
@@ -499,36 +406,6 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
     for (; it0 <= ntiles; it0 += 2) {
       step(it0, std::integral_constant<int, 1>{}, std::true_type{});
       if (it0 + 1 <= ntiles) step(it0 + 1, std::integral_constant<int, 0>{}, std::true_type{});
-    }
-  } else {
-    // One tile per step in sequence (scores, softmax, PV); K(j+1) and V(j+1)
-    // load into the other buffers meanwhile.
-    auto step = [&](int it, auto U) {
-      constexpr int u = decltype(U)::value;
-      const int j0 = it * BN;
-      if (it + 1 < ntiles) {
-        load_k(j0 + BN, kbuf(std::integral_constant<int, u + 1>{}));
-        load_v(j0 + BN, vbuf(std::integral_constant<int, u + 1>{}));
-      }
-      if (it < ntw) {
-        f32x16 sc[RG][NH];
-        scores(kbuf(std::integral_constant<int, u>{}), sc);
-        mask_and_rescale(j0, sc, std::true_type{});
-        bf16x8 pk[RG][NH][2];
-        probabilities(sc, pk);
-        pv(vbuf(std::integral_constant<int, u>{}), pk);
-      }
-      pipeline_barrier<0>();
-    };
-    if (ntiles > 0) {
-      load_k(0, kb0);
-      load_v(0, vb0);
-    }
-    pipeline_barrier<0>();
-    for (int it0 = 0; it0 < ntiles; it0 += 2) {
-      static_for<0, 2>([&](auto U) {
-        if (it0 + U < ntiles) step(it0 + U, U);
-      });
     }
   }
 
