@@ -24,7 +24,7 @@ resident in device memory before the timed region.  Prints ONE JSON line:
              d64): the fp32 weight matrix written per second; the weights
              kernel's time is the call's minus attn_fwd_lse's (both HIP events)
   mha        the multi-head wrapper (attn_mha_fwd) on B32 T1024 d_model 512 h8:
-             projection GEMMs (rocBLAS) + head moves + attention + W^O GEMM;
+             weight transpose + projection GEMM + strided attention + W^O GEMM;
              TFLOP/s counts 2*B*d_model^2*(2 Tq + 2 Tk) projection flops plus the
              attention's 4*B*h*Tq*Tk*d
   backward   (bf16 workloads) the gradient pass on the same inputs: attn_bwd
@@ -352,7 +352,7 @@ def time_mha(torch, tsd, name, steps, warmup):
     att = 4.0 * B * h * Tq * Tk * d / (2 if c["causal"] else 1)
     return {
         "workload": name,
-        "what": "attn_mha_fwd: fused QKV projection (rocBLAS), strided attention, W^O projection (rocBLAS)",
+        "what": "attn_mha_fwd: weight transpose, fused QKV projection GEMM, strided attention, W^O projection GEMM",
         "ms": round(ms, 4),
         "flops_per_step": proj + att,
         "tflops": round((proj + att) / (ms * 1e-3) / 1e12, 2),

@@ -79,7 +79,6 @@ enum {
   ATTN_ERR_TOO_LARGE = -8,   /* more than 2^31-1 work-groups, or one head's rows of a tensor
                                 exceed 4 GiB (T * d * element size >= 2^32) */
   ATTN_ERR_WORKSPACE = -9,   /* workspace NULL or smaller than the *_workspace_bytes() figure */
-  ATTN_ERR_BLAS = -10,       /* attn_mha_fwd: a rocBLAS GEMM failed (rocblas_status in attn_last_hip_error()) */
   ATTN_ERR_HIP = -100        /* the kernel launch failed; see attn_last_hip_error() */
 };
 
@@ -241,14 +240,13 @@ size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d);
  *             attn_mha_workspace_bytes(B, Tq, Tk, d_model) bytes, 256-byte
  *             aligned, overlapping no tensor; no initialisation needed; calls
  *             that share it must not overlap in time
- * The projections are rocBLAS GEMMs (bf16 operands, fp32 accumulation, bf16
- * results: the projected Q, K, V and the merged heads are rounded to bf16),
- * pointed at a slice of the workspace; the head moves and the attention are
- * this library's kernels.  All work is enqueued on `stream`.  The first call
- * on a device creates that device's rocBLAS handle (rocBLAS's own set-up),
- * kept until the process ends; calls are serialised on it.
- * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE and ATTN_ERR_BLAS.  B or Tq = 0
- * is a no-op; Tk = 0 gives y = 0.
+ * The projections are this library's GEMM kernel (bf16 operands, fp32
+ * accumulation, bf16 results: the projected Q, K, V and the merged heads are
+ * rounded to bf16); the attention reads the projections in place.  All work is
+ * enqueued on `stream`; nothing is allocated.
+ * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE, and ATTN_ERR_TOO_LARGE when
+ * B * max(Tq, Tk) exceeds 2^31 - 1 rows.  B or Tq = 0 is a no-op; Tk = 0 gives
+ * y = 0.
  */
 int attn_mha_fwd(const void* xq, const void* xk, const void* xv,
                  const void* wq, const void* wk, const void* wv, const void* wo, void* y,

@@ -19,7 +19,7 @@ by libattn.so.
 """
 from ._lib import (  # noqa: F401
     ERR_ALIAS, ERR_ALIGN, ERR_HEADDIM, ERR_HIP, ERR_MASK, ERR_NULL, ERR_SCALE, ERR_SHAPE,
-    ERR_BLAS, ERR_TOO_LARGE, ERR_WORKSPACE, LIB_PATH, MASK_CAUSAL, MASK_KEYPAD, MASK_NONE, OK, LibraryMissing,
+    ERR_TOO_LARGE, ERR_WORKSPACE, LIB_PATH, MASK_CAUSAL, MASK_KEYPAD, MASK_NONE, OK, LibraryMissing,
     attn_bwd, attn_decode, attn_decode_workspace_bytes, attn_fwd, attn_fwd_f32, attn_fwd_lse, attn_fwd_weights, attn_last_hip_error, attn_mha_fwd, attn_mha_workspace_bytes, attn_status_str, attn_version, raw_library,
 )
 from .ops import (AttentionError, AttentionFunction, attention, attention_backward, attention_lse,  # noqa: F401

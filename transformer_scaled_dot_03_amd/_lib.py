@@ -27,7 +27,6 @@ ERR_ALIGN = -6
 ERR_SCALE = -7
 ERR_TOO_LARGE = -8
 ERR_WORKSPACE = -9
-ERR_BLAS = -10
 ERR_HIP = -100
 
 # names and C signatures of every exported entry point (kept in step with attn.h)

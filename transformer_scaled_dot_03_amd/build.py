@@ -20,9 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_mha.hip", "attn_api.hip"]
-# libraries each target links (the multi-head wrapper's projections are rocBLAS GEMMs)
-LINK = {"libattn.so": ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib", "-lrocblas"]}
+SOURCES = ["attn_fwd_kernel.hip", "attn_bwd_kernel.hip", "attn_decode_kernel.hip", "attn_gemm_kernel.hip",
+           "attn_mha.hip", "attn_api.hip"]
+# libraries each target links beyond the HIP runtime
+LINK: dict[str, list[str]] = {}
 # measurement aid for the benchmark: pure matrix-core loop (include/mfma_probe.h)
 PROBE_LIB_PATH = os.path.join(PKG, "libmfma_probe.so")
 PROBE_SOURCES = ["mfma_probe.hip"]

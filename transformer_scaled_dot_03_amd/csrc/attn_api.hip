@@ -245,9 +245,10 @@ int mha_fwd(const void* xq, const void* xk, const void* xv, const void* wq, cons
   if (misaligned(workspace, 256) || (Tk > 0 && (misaligned(xk, 16) || misaligned(xv, 16))))
     return ATTN_ERR_ALIGN;
   if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
-  // rocBLAS takes 32-bit sizes; one head's rows (stride up to 3 d_model) sit behind a 32-bit range
+  // the GEMMs take B T rows as a 32-bit count; one head's rows (stride up to
+  // 3 d_model) sit behind a 32-bit buffer range in the attention kernel
   const int64_t tmax = Tq > Tk ? Tq : Tk;
-  if (static_cast<int64_t>(B) * tmax * 3 * d_model > 0x7fffffffLL || tmax * 3 * d_model * 2 > 0xffffffffLL)
+  if (static_cast<int64_t>(B) * tmax > 0x7fffffffLL || tmax * 3 * d_model * 2 > 0xffffffffLL)
     return ATTN_ERR_TOO_LARGE;
   const int64_t bm = attn::rows_per_block(attn::DType::BF16, d);
   const int64_t n_qtiles = (Tq + bm - 1) / bm;
@@ -294,15 +295,9 @@ int mha_fwd(const void* xq, const void* xk, const void* xv, const void* wq, cons
   p.n_qtiles = static_cast<int>(n_qtiles);
   p.n_wg = static_cast<int>(static_cast<int64_t>(B) * h * n_qtiles);
   p.lse = nullptr;
-  int blas_status = 0;
-  hipError_t hip_status = hipSuccess;
-  const int r = attn::mha_run(a, stream, &blas_status, &hip_status);
-  if (r == -2) {
-    g_last_hip_error = blas_status;
-    return ATTN_ERR_BLAS;
-  }
-  if (r != 0) {
-    g_last_hip_error = static_cast<int>(hip_status);
+  const hipError_t e = attn::mha_run(a, stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
@@ -451,7 +446,6 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_bytes()";
-    case ATTN_ERR_BLAS: return "rocBLAS GEMM failed (see attn_last_hip_error for the rocblas_status)";
     case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";

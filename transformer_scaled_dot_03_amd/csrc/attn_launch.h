@@ -81,16 +81,40 @@ struct WtsParams {
 int weights_rows_per_block(int d);
 hipError_t launch_weights(const WtsParams& p, int d, bool causal, bool keypad, hipStream_t stream);
 
-// Multi-head attention forward (projections through rocBLAS, attention here,
-// reading the projections in place through strides).  Workspace layout, byte
-// offsets from its start.
-constexpr size_t kMhaBlasWorkspace = size_t(32) << 20;   // handed to rocBLAS
+// Projection GEMM of the multi-head wrapper: C[M x N] = A[M x K] B[K x N],
+// bf16 operands and result, fp32 accumulation.  A is row-major [M x K], B is
+// passed transposed (bt = B^T, row-major [N x K]), C row-major [M x N];
+// leading dimensions in elements.  K a multiple of 64, N of 8; lda, ldb, ldc
+// multiples of 8 (16-byte rows); pointers 16-byte aligned.
+struct GemmParams {
+  const void* a;
+  const void* bt;
+  void* c;
+  int M, N, K;
+  int lda, ldb, ldc;
+  int n_mt, n_nt;           // row and column tiles of C (set by launch_gemm)
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t stream);
+
+// dst [C x R] = src [R x C]^T (bf16) for up to four matrices in one launch;
+// R and C multiples of 64
+struct TransposeJob {
+  const __bf16* src;
+  __bf16* dst;
+};
+struct TransposeJobs {
+  TransposeJob job[4];
+  int R, C;
+};
+hipError_t launch_transpose(const TransposeJobs& J, int njobs, hipStream_t stream);
+
+// Multi-head attention forward (projection GEMMs, attention reading the
+// projections in place through strides, output projection).  Workspace
+// layout, byte offsets from its start.
 struct MhaLayout {
-  size_t wcat;        // bf16 [d_model, 3 d_model]: [Wq | Wk | Wv] (self-attention)
+  size_t wt;          // bf16 [4 d_model, d_model]: Wq^T, Wk^T, Wv^T, Wo^T (the GEMMs' B^T operands)
   size_t proj;        // bf16: [B T, 3 d_model] (self) or [B Tq, d_model] + [B Tk, 2 d_model] (cross)
   size_t o;           // bf16 [B, Tq, h, d]: the attention output, heads side by side
-  size_t blas;        // rocBLAS workspace
-  size_t blas_bytes;
   size_t bytes;       // total
 };
 MhaLayout mha_layout(int B, int Tq, int Tk, int d_model);
@@ -102,11 +126,11 @@ struct MhaArgs {
   void* workspace;
   int B, Tq, Tk, d_model, H, D;
   bool causal, keypad;
-  bool fused_qkv;             // xq == xk == xv: one projection GEMM with [Wq | Wk | Wv]
+  bool fused_qkv;             // xq == xk == xv: one projection GEMM against [Wq | Wk | Wv]
   Params attn;                // scale, mask and tiling of the attention launch
 };
-// 0 on success; -1: a HIP launch failed (*hip_status); -2: rocBLAS failed (*blas_status)
-int mha_run(const MhaArgs& a, hipStream_t stream, int* blas_status, hipError_t* hip_status);
+// hipSuccess, or the first launch error
+hipError_t mha_run(const MhaArgs& a, hipStream_t stream);
 
 // Decode (one query row per (b, head)) split over the keys: arguments of the
 // split kernel and of the merge kernel.
