@@ -72,6 +72,15 @@ def test_mha_self_attention(tsd, dm, h, mask):
     _run_check(tsd, 2, T, T, dm, h, causal=mask == "causal", key_lens=[120, T] if mask == "keypad" else None)
 
 
+# d_model not a multiple of 256: the projection GEMM's last column tile is partly
+# (N = 576, 960) or, for one of its two 128-column halves, wholly (N = 1152) past N, and
+# K = d_model gives an odd number of 64-wide k steps (192, 320)
+@pytest.mark.parametrize("dm,h", [(192, 3), (320, 5), (384, 3)])
+def test_mha_projection_tile_edges(tsd, dm, h):
+    _run_check(tsd, 2, 300, 300, dm, h, seed=dm)
+    _run_check(tsd, 3, 45, 270, dm, h, cross=True, seed=dm + 1)
+
+
 @pytest.mark.parametrize("Tq,Tk", [(77, 130), (1, 300), (130, 65)])
 def test_mha_cross_attention(tsd, Tq, Tk):
     _run_check(tsd, 3, Tq, Tk, 512, 8, cross=True, seed=Tq + Tk)
