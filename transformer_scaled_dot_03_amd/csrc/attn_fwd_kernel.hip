@@ -275,6 +275,10 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
               sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
             }
       }
+      // IEEE maximum (NaN-propagating): gfx950's v_maximum3_f32, with no
+      // canonicalising moves in front of it (a NaN score makes the row NaN
+      // through its exponential either way)
+      auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
       bool grow = false;
 #pragma unroll
       for (int r = 0; r < RG; ++r) {
@@ -284,8 +288,10 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, 3 - Bf16Shape<D>::kRG) v
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) mx[(2 * hh + e / 8) % 4] = fmaxf(mx[(2 * hh + e / 8) % 4], sc[r][hh][e]);
-        m_tile[r] = pair_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * cs;
+          for (int e = 0; e < 16; ++e) mx[(2 * hh + e / 8) % 4] = vmax(mx[(2 * hh + e / 8) % 4], sc[r][hh][e]);
+        const float m4 = vmax(vmax(mx[0], mx[1]), vmax(mx[2], mx[3]));
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4), __float_as_uint(m4), false, false);
+        m_tile[r] = vmax(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * cs;
         grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
       }
       return grow;
