@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -244,15 +246,15 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void attn_gemm_bf16_kernel(Gemm
 // compute units of the current device (the persistent grid size), cached per device
 static int device_cus() {
   constexpr int kMaxDev = 64;
-  static int cus[kMaxDev] = {};
+  static std::atomic<int> cus[kMaxDev];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;   // same value from any thread
+    cus[dev].store(n, std::memory_order_relaxed);   // every thread stores the same value
   }
-  return cus[dev];
+  return n;
 }
 
 hipError_t launch_gemm(const GemmParams& p0, hipStream_t stream) {
