@@ -81,6 +81,12 @@ def test_mha_projection_tile_edges(tsd, dm, h):
     _run_check(tsd, 3, 45, 270, dm, h, cross=True, seed=dm + 1)
 
 
+def test_mha_many_projection_tiles_ragged(tsd):
+    # B Tq = 90003 query rows: the Q and W^O projections have far more 256 x 256 tiles
+    # than the GPU has CUs (work-groups loop over tiles) and a ragged last row block
+    _run_check(tsd, 3, 30001, 70, 512, 8, cross=True, seed=11)
+
+
 @pytest.mark.parametrize("Tq,Tk", [(77, 130), (1, 300), (130, 65)])
 def test_mha_cross_attention(tsd, Tq, Tk):
     _run_check(tsd, 3, Tq, Tk, 512, 8, cross=True, seed=Tq + Tk)
