@@ -28,10 +28,10 @@
 //
 // Rows of A past M and rows of B^T past N read as zero through the buffer
 // range check; rows of C past M and columns past N are not written.  A K-step
-// of 64 reads 64 KB from L2 per work-group and feeds 256 MFMAs (8 per 1 KB
-// of LDS read per wave and slice): measured on MI355X the step runs at the
-// matrix-core rate; what remains is the prologue of each tile and the burst
-// of output stores that all CUs issue together.
+// of 64 reads 64 KB from L2 per work-group and feeds 256 MFMAs (per wave and
+// 16-k slice: 6 KB of fragment reads for 8 MFMAs): measured on MI355X the step
+// runs at the matrix-core rate; what remains is the prologue of each tile and
+// the burst of output stores that all CUs issue together.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
