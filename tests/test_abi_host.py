@@ -351,6 +351,8 @@ def test_mha_workspace_size(L):
     (dict(y=0x10000000 + 512), "ERR_ALIAS"),  # y inside xq
     (dict(ws=0x30000000), "ERR_ALIAS"),       # workspace on wk
     (dict(y=0x80000000 + 4096), "ERR_ALIAS"), # y inside the workspace
+    (dict(B=70000, Tq=40000, Tk=40000), "ERR_TOO_LARGE"),   # B T rows past 2^31 - 1
+    (dict(Tq=1 << 21, Tk=1 << 21), "ERR_TOO_LARGE"),        # one head's projected rows past 4 GiB
 ])
 def test_mha_bad_arguments_rejected_before_any_launch(L, over, code):
     assert _call_mha(L, **over) == getattr(L, code)
