@@ -72,7 +72,8 @@ enum {
   ATTN_ERR_SHAPE = -2,       /* negative dimension, or d_k != d_v */
   ATTN_ERR_HEADDIM = -3,     /* head size not supported (supported: 64, 128) */
   ATTN_ERR_MASK = -4,        /* unknown mask bits, or KEYPAD with key_lens == NULL */
-  ATTN_ERR_ALIAS = -5,       /* an output buffer overlaps an input or another output */
+  ATTN_ERR_ALIAS = -5,       /* an output buffer (or workspace) overlaps an input, another
+                                output or, under key padding, key_lens[0 .. B) */
   ATTN_ERR_ALIGN = -6,       /* a bf16/fp32 tensor not 16-byte aligned; key_lens, lse or delta
                                 not 4-byte aligned */
   ATTN_ERR_SCALE = -7,       /* scale is NaN or infinite */

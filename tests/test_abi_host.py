@@ -3,6 +3,14 @@
 The library must load, export every entry point include/attn.h declares, and
 reject bad arguments with the documented status before any HIP call (the
 pointers below are never dereferenced; these calls make no HIP call at all).
+
+The calls pass made-up device addresses.  Where a GPU is visible, a
+regressed check would launch a kernel on them, so there the tests of this
+file run only in a child process that sees no GPU (test_abi_isolated.py
+starts it with HIP_VISIBLE_DEVICES empty): a launch then fails with
+ATTN_ERR_HIP instead of touching memory.  The same child mode runs them
+against a build of the library whose host code is instrumented with
+AddressSanitizer and UndefinedBehaviorSanitizer (ATTN_ABI_TEST_LIB).
 """
 from __future__ import annotations
 
@@ -16,11 +24,38 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
+# set by test_abi_isolated.py in the child processes it starts
+CHILD = os.environ.get("ATTN_ABI_HOST_CHILD") == "1"
+GPU_NODE = os.path.exists("/dev/kfd")
+
+pytestmark = pytest.mark.skipif(
+    GPU_NODE and not CHILD,
+    reason="a GPU is visible: these fake-address calls run in a GPU-less child (test_abi_isolated.py)")
+
+
+def _visible_gpus() -> int:
+    """Devices the HIP runtime reports in this process (0 if it reports an error)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    n = ctypes.c_int(0)
+    return n.value if hip.hipGetDeviceCount(ctypes.byref(n)) == 0 else 0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def no_gpu_in_child():
+    """In the child on a GPU host, refuse to run if the runtime still sees a device."""
+    if CHILD and GPU_NODE and _visible_gpus() != 0:
+        pytest.exit("HIP_VISIBLE_DEVICES did not hide the GPU: not running fake-address calls", returncode=3)
+
 
 @pytest.fixture(scope="module")
 def L():
     from transformer_scaled_dot_03_amd import _lib
-    if not os.path.exists(_lib.LIB_PATH):
+    other = os.environ.get("ATTN_ABI_TEST_LIB")
+    if other:
+        # a differently built copy of the library (the sanitizer build)
+        _lib.LIB_PATH = other
+        _lib._lib = None
+    elif not os.path.exists(_lib.LIB_PATH):
         from transformer_scaled_dot_03_amd import build
         build.build()
     return _lib

@@ -60,12 +60,14 @@ int fwd(attn::DType dt, const void* q, const void* k, const void* v, void* out, 
   typedef unsigned __int128 u128;
   const u128 es = dt == attn::DType::F32 ? 4 : 2;
   const u128 nq = (u128)bh * Tq * d_k * es, nkv = (u128)bh * Tk * d_k * es, no = (u128)bh * Tq * d_v * es;
-  if (overlaps(out, no, q, nq) || overlaps(out, no, k, nkv) || overlaps(out, no, v, nkv))
+  const u128 nkl = keypad ? (u128)B * 4 : 0;   // key_lens is read by every work-group
+  if (overlaps(out, no, q, nq) || overlaps(out, no, k, nkv) || overlaps(out, no, v, nkv) ||
+      overlaps(out, no, key_lens, nkl))
     return ATTN_ERR_ALIAS;
   if (lse != nullptr) {
     const u128 nl = (u128)bh * Tq * 4;
     if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
-        overlaps(lse, nl, out, no))
+        overlaps(lse, nl, out, no) || overlaps(lse, nl, key_lens, nkl))
       return ATTN_ERR_ALIAS;
   }
 
@@ -131,12 +133,12 @@ int bwd(const void* q, const void* k, const void* v, const void* out, const void
   typedef unsigned __int128 u128;
   const u128 nq = rows ? (u128)bh * Tq * d_k * 2 : 0, nkv = keys ? (u128)bh * Tk * d_k * 2 : 0;
   const u128 nr = rows ? (u128)bh * Tq * 4 : 0;   // lse; delta holds two such arrays
-  const void* in_p[6] = {q, k, v, out, dout, lse};
-  const u128 in_n[6] = {nq, nkv, nkv, nq, nq, nr};
+  const void* in_p[7] = {q, k, v, out, dout, lse, key_lens};
+  const u128 in_n[7] = {nq, nkv, nkv, nq, nq, nr, keypad ? (u128)B * 4 : 0};
   const void* out_p[4] = {delta, dq, dk, dv};
   const u128 out_n[4] = {2 * nr, nq, nkv, nkv};
   for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
+    for (int j = 0; j < 7; ++j)
       if (overlaps(out_p[i], out_n[i], in_p[j], in_n[j])) return ATTN_ERR_ALIAS;
     for (int j = i + 1; j < 4; ++j)
       if (overlaps(out_p[i], out_n[i], out_p[j], out_n[j])) return ATTN_ERR_ALIAS;
@@ -192,9 +194,9 @@ int fwd_weights(const void* q, const void* k, const void* v, void* out, float* l
     typedef unsigned __int128 u128;
     const u128 bh = (u128)B * h;
     const u128 nw = bh * Tq * Tk * 4, nq = bh * Tq * d_k * 2, nkv = bh * Tk * d_k * 2, no = bh * Tq * d_v * 2;
-    const u128 nl = bh * Tq * 4;
+    const u128 nl = bh * Tq * 4, nkl = (mask_kind & ATTN_MASK_KEYPAD) ? (u128)B * 4 : 0;
     if (overlaps(weights, nw, q, nq) || overlaps(weights, nw, k, nkv) || overlaps(weights, nw, v, nkv) ||
-        overlaps(weights, nw, out, no) || overlaps(weights, nw, lse, nl))
+        overlaps(weights, nw, out, no) || overlaps(weights, nw, lse, nl) || overlaps(weights, nw, key_lens, nkl))
       return ATTN_ERR_ALIAS;
   }
   const int st = fwd(attn::DType::BF16, q, k, v, out, lse, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens,
@@ -259,9 +261,9 @@ int mha_fwd(const void* xq, const void* xk, const void* xv, const void* wq, cons
   typedef unsigned __int128 u128;
   const u128 row = (u128)d_model * 2, hw = (u128)d_model * d_model * 2;
   const u128 nxq = (u128)B * Tq * row, nxkv = (u128)B * Tk * row, ny = nxq, nw = L.bytes;
-  const void* in_p[7] = {xq, xk, xv, wq, wk, wv, wo};
-  const u128 in_n[7] = {nxq, nxkv, nxkv, hw, hw, hw, hw};
-  for (int j = 0; j < 7; ++j)
+  const void* in_p[8] = {xq, xk, xv, wq, wk, wv, wo, key_lens};
+  const u128 in_n[8] = {nxq, nxkv, nxkv, hw, hw, hw, hw, keypad ? (u128)B * 4 : 0};
+  for (int j = 0; j < 8; ++j)
     if (overlaps(y, ny, in_p[j], in_n[j]) || overlaps(workspace, nw, in_p[j], in_n[j])) return ATTN_ERR_ALIAS;
   if (overlaps(y, ny, workspace, nw)) return ATTN_ERR_ALIAS;
 
@@ -345,9 +347,10 @@ int decode(const void* q, const void* k, const void* v, void* out, int B, int h,
 
   typedef unsigned __int128 u128;
   const u128 nq = (u128)bh * d_k * 2, nkv = (u128)bh * Tk * d_k * 2, nw = ws.bytes;
+  const u128 nkl = keypad ? (u128)B * 4 : 0;
   if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nkv) || overlaps(out, nq, v, nkv) ||
-      overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) || overlaps(workspace, nw, v, nkv) ||
-      overlaps(workspace, nw, out, nq))
+      overlaps(out, nq, key_lens, nkl) || overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) ||
+      overlaps(workspace, nw, v, nkv) || overlaps(workspace, nw, out, nq) || overlaps(workspace, nw, key_lens, nkl))
     return ATTN_ERR_ALIAS;
 
   attn::DecParams p;
@@ -445,7 +448,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
-    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_decode_workspace_bytes()";
+    case ATTN_ERR_WORKSPACE:
+      return "workspace missing or smaller than attn_decode_workspace_bytes() / attn_mha_workspace_bytes()";
     case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";

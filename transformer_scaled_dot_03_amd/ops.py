@@ -41,19 +41,26 @@ def _check_qkv(q, k, v, dtypes):
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in dtypes:
         raise TypeError("q, k, v must share one dtype out of " + ", ".join(str(d) for d in dtypes))
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError(f"{name} must be a device tensor on q's device")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     return B, h, Tq, Tk, dk, dv
 
 
-def _mask_args(B, causal, key_lens):
+def _on_device(t, device) -> bool:
+    """True when t lives in the memory of the GPU `device` (a CPU tensor's address
+    would pass every check of the C ABI and then be written by a kernel)."""
+    return t.is_cuda and t.device == torch.device(device)
+
+
+def _mask_args(B, causal, key_lens, device):
     mask = _lib.MASK_CAUSAL if causal else _lib.MASK_NONE
     kl_ptr = None
     if key_lens is not None:
-        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.shape != (B,):
-            raise ValueError("key_lens must be an int32 [B] device tensor")
+        if (key_lens.dtype != torch.int32 or tuple(key_lens.shape) != (B,) or not key_lens.is_contiguous()
+                or not _on_device(key_lens, device)):
+            raise ValueError("key_lens must be a contiguous int32 [B] tensor on the inputs' device")
         mask |= _lib.MASK_KEYPAD
         kl_ptr = key_lens.data_ptr()
     return mask, kl_ptr
@@ -62,8 +69,8 @@ def _mask_args(B, causal, key_lens):
 def _out_like(t, shape, dtype, device, name):
     if t is None:
         return torch.empty(shape, dtype=dtype, device=device)
-    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous {tuple(shape)} {dtype} tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous() or not _on_device(t, device):
+        raise ValueError(f"{name} must be a contiguous {tuple(shape)} {dtype} tensor on {device}")
     return t
 
 
@@ -81,7 +88,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     """
     B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16, torch.float32))
     out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
-    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
@@ -99,7 +106,7 @@ def attention_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     B, h, Tq, Tk, dk, dv = _check_qkv(q, k, v, (torch.bfloat16,))
     out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
     lse = _out_like(lse, (B, h, Tq), torch.float32, q.device, "lse")
-    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
@@ -120,7 +127,7 @@ def attention_weights(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
     out = _out_like(out, (B, h, Tq, dv), q.dtype, q.device, "out")
     lse = _out_like(lse, (B, h, Tq), torch.float32, q.device, "lse")
     weights = _out_like(weights, (B, h, Tq, Tk), torch.float32, q.device, "weights")
-    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
@@ -145,15 +152,17 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     """
     B, h, Tq, Tk, d_k, d_v = _check_qkv(q, k, v, (torch.bfloat16,))
     for name, t, shape in (("out", out, (B, h, Tq, d_v)), ("dout", dout, (B, h, Tq, d_v))):
-        if tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous bf16 device tensor of shape {shape}")
-    if tuple(lse.shape) != (B, h, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 [B, h, Tq] tensor")
+        if (tuple(t.shape) != shape or t.dtype != torch.bfloat16 or not t.is_contiguous()
+                or not _on_device(t, q.device)):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {shape} on q's device")
+    if (tuple(lse.shape) != (B, h, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or not _on_device(lse, q.device)):
+        raise ValueError("lse must be a contiguous fp32 [B, h, Tq] tensor on q's device")
     dq = _out_like(dq, q.shape, q.dtype, q.device, "dq")
     dk = _out_like(dk, k.shape, k.dtype, k.device, "dk")
     dv = _out_like(dv, v.shape, v.dtype, v.device, "dv")
     delta = _out_like(delta, (2, B, h, Tq), torch.float32, q.device, "delta")
-    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(d_k)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
@@ -198,12 +207,12 @@ def decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: f
     if Tq != 1:
         raise ValueError("decode_attention takes one query row per (b, head): q must be [B, h, 1, d]")
     out = _out_like(out, (B, h, 1, dv), q.dtype, q.device, "out")
-    mask, kl_ptr = _mask_args(B, False, key_lens)
+    mask, kl_ptr = _mask_args(B, False, key_lens, q.device)
     need = _lib.attn_decode_workspace_bytes(B, h, Tk, dk) if B > 0 and h > 0 else 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not _on_device(workspace, q.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     if scale is None:
         scale = default_scale(dk)
     st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
@@ -231,8 +240,8 @@ def multi_head_attention(xq: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, w
     xv = xk if xv is None else xv
     ts = (("xq", xq), ("xk", xk), ("xv", xv), ("wq", wq), ("wk", wk), ("wv", wv), ("wo", wo))
     for name, t in ts:
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous bf16 device tensor")
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or not _on_device(t, xq.device):
+            raise ValueError(f"{name} must be a contiguous bf16 tensor on xq's device")
     if xq.dim() != 3 or xk.dim() != 3 or xv.shape != xk.shape:
         raise ValueError("xq must be [B, Tq, d_model] and xk, xv [B, Tk, d_model]")
     B, Tq, dm = xq.shape
@@ -243,12 +252,12 @@ def multi_head_attention(xq: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, w
         if tuple(w.shape) != (dm, dm):
             raise ValueError(f"{name} must be [d_model, d_model]")
     out = _out_like(out, (B, Tq, dm), torch.bfloat16, xq.device, "out")
-    mask, kl_ptr = _mask_args(B, causal, key_lens)
+    mask, kl_ptr = _mask_args(B, causal, key_lens, xq.device)
     need = _lib.attn_mha_workspace_bytes(B, Tq, Tk, dm)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
-    elif workspace.dtype != torch.uint8 or not workspace.is_cuda or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous uint8 device tensor")
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous() or not _on_device(workspace, xq.device):
+        raise ValueError("workspace must be a contiguous uint8 tensor on xq's device")
     if scale is None:
         scale = default_scale(dm // heads) if heads > 0 and dm % heads == 0 else 1.0
     st = (stream if stream is not None else torch.cuda.current_stream(xq.device)).cuda_stream
