@@ -222,6 +222,29 @@ int attn_decode(const void* q, const void* k, const void* v, void* out,
 size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d);
 
 /*
+ * attn_decode_static: attn_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The per-split partials go
+ * to a static device array of the library, ATTN_DECODE_STATIC_SCRATCH_BYTES
+ * bytes on each GPU the library runs on, held until the process ends; its
+ * address is looked up once per device (on the first call with that device
+ * current).  The call allocates nothing.
+ *   Arguments, results and errors as attn_decode; in addition
+ *   ATTN_ERR_WORKSPACE when attn_decode_workspace_bytes(B, h, Tk, d) exceeds
+ *   ATTN_DECODE_STATIC_SCRATCH_BYTES (returned before any HIP call), and
+ *   ATTN_ERR_HIP (hipErrorInvalidDevice) when `stream` belongs to another
+ *   device than the current one.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap in
+ * time on one GPU (different streams, not synchronised) race and give wrong
+ * results; calls in order on one stream are safe.  Nothing in the array needs
+ * to start at zero: the split kernel writes every partial the merge reads.
+ */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_static(const void* q, const void* k, const void* v, void* out,
+                       int B, int h, int Tk, int d_k, int d_v, float scale,
+                       int mask_kind, const int32_t* key_lens, hipStream_t stream);
+
+/*
  * attn_mha_fwd: multi-head attention forward,
  *
  *     MultiHead = Concat(head_1, ..., head_h) W^O,

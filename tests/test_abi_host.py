@@ -75,7 +75,7 @@ def _declared_enum():
 def test_header_declares_expected_entry_points():
     assert _declared_functions() == sorted(
         ["attn_fwd", "attn_fwd_f32", "attn_fwd_lse", "attn_fwd_weights", "attn_bwd", "attn_decode",
-         "attn_decode_workspace_bytes", "attn_mha_fwd", "attn_mha_workspace_bytes",
+         "attn_decode_static", "attn_decode_workspace_bytes", "attn_mha_fwd", "attn_mha_workspace_bytes",
          "attn_status_str", "attn_last_hip_error", "attn_version"])
 
 
@@ -146,6 +146,7 @@ def _call(L, f32=False, **over):
     (dict(v=V + 4), "ERR_ALIGN"),
     (dict(out=O + 12), "ERR_ALIGN"),
     (dict(mask_kind=2, key_lens=KL + 2), "ERR_ALIGN"),
+    (dict(mask_kind=2, key_lens=O + 64), "ERR_ALIAS"),   # out overlaps key_lens
     (dict(out=Q), "ERR_ALIAS"),
     (dict(out=K + 4096), "ERR_ALIAS"),
     (dict(out=V - 16), "ERR_ALIAS"),
@@ -182,6 +183,7 @@ def _call_lse(L, **over):
     (dict(lse=LSE + 2), "ERR_ALIGN"),
     (dict(lse=O + 64), "ERR_ALIAS"),
     (dict(lse=Q), "ERR_ALIAS"),
+    (dict(mask_kind=2, key_lens=LSE + 8), "ERR_ALIAS"),   # lse overlaps key_lens
     (dict(d_k=32, d_v=32), "ERR_HEADDIM"),
     (dict(mask_kind=2), "ERR_MASK"),
     (dict(scale=float("nan")), "ERR_SCALE"),
@@ -214,6 +216,7 @@ def _call_wts(L, **over):
     (dict(weights=Q + 1024), "ERR_ALIAS"),
     (dict(weights=LSE - 64), "ERR_ALIAS"),       # its first bytes run into lse
     (dict(weights=O), "ERR_ALIAS"),
+    (dict(mask_kind=2, key_lens=WTS + 1024), "ERR_ALIAS"),   # weights overlap key_lens
     (dict(d_k=32, d_v=32, weights=None), "ERR_HEADDIM"),   # the forward's checks come first
     (dict(mask_kind=5), "ERR_MASK"),
     (dict(scale=float("inf")), "ERR_SCALE"),
@@ -275,6 +278,7 @@ def _call_bwd(L, **over):
     (dict(delta=0x60000000 + 16), "ERR_ALIAS"), # delta inside lse
     (dict(dv=0x50000000), "ERR_ALIAS"),         # dv on dout
     (dict(delta=0xA0000000 + 128), "ERR_ALIAS"),
+    (dict(mask_kind=2, key_lens=0x80000000 + 4), "ERR_ALIAS"),   # dq overlaps key_lens
     (dict(B=1 << 30, h=1 << 10, Tq=1 << 20), "ERR_TOO_LARGE"),
     (dict(B=1, h=1, Tq=1 << 24, d_k=128, d_v=128), "ERR_TOO_LARGE"),   # one head's Q: 4 GiB
 ])
@@ -332,6 +336,7 @@ def test_decode_workspace_size(L):
     (dict(out=0x40000004), "ERR_ALIGN"),
     (dict(ws=0x20000000 + 4096), "ERR_ALIAS"),  # workspace inside k
     (dict(out=0x10000000), "ERR_ALIAS"),
+    (dict(mask_kind=2, key_lens=0x50000000 + 64), "ERR_ALIAS"),   # the workspace overlaps key_lens
     (dict(Tk=1 << 25), "ERR_TOO_LARGE"),
 ])
 def test_decode_bad_arguments_rejected_before_any_launch(L, over, code):
@@ -342,6 +347,50 @@ def test_decode_bad_arguments_rejected_before_any_launch(L, over, code):
 def test_decode_empty_is_a_no_op(L):
     assert _call_dec(L, B=0, q=None, out=None, ws=None) == L.OK
     assert _call_dec(L, h=0) == L.OK
+
+
+def _call_dec_static(L, **over):
+    a = dict(DEC)
+    a.update(over)
+    return L.attn_decode_static(a["q"], a["k"], a["v"], a["out"], a["B"], a["h"], a["Tk"], a["d_k"], a["d_v"],
+                                a["scale"], a["mask_kind"], a["key_lens"], a["stream"])
+
+
+def test_decode_static_scratch_size_matches_header(L):
+    m = re.search(r"#define ATTN_DECODE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == L.DECODE_STATIC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), "ERR_SHAPE"),
+    (dict(d_v=64), "ERR_SHAPE"),
+    (dict(d_k=80, d_v=80), "ERR_HEADDIM"),
+    (dict(mask_kind=1), "ERR_MASK"),
+    (dict(mask_kind=2), "ERR_MASK"),
+    (dict(scale=float("inf")), "ERR_SCALE"),
+    (dict(q=None), "ERR_NULL"),
+    (dict(v=None), "ERR_NULL"),
+    (dict(out=0x40000004), "ERR_ALIGN"),
+    (dict(out=0x20000000 + 256), "ERR_ALIAS"),   # out inside k
+    (dict(mask_kind=2, key_lens=0x40000000), "ERR_ALIAS"),   # out on key_lens
+    (dict(Tk=1 << 25), "ERR_TOO_LARGE"),
+    # more partials than the static array holds: one per (b, head) already exceeds 16 MiB
+    (dict(B=1024, h=64, Tk=1, d_k=64, d_v=64), "ERR_WORKSPACE"),
+])
+def test_decode_static_bad_arguments_rejected_before_any_hip_call(L, over, code):
+    assert _call_dec_static(L, **over) == getattr(L, code)
+    assert L.attn_last_hip_error() == 0
+
+
+def test_decode_static_limit_is_the_workspace_size(L):
+    # the largest problems it takes are exactly those whose attn_decode workspace fits the array
+    assert L.attn_decode_workspace_bytes(8, 16, 16384, 128) <= L.DECODE_STATIC_SCRATCH_BYTES
+    assert L.attn_decode_workspace_bytes(1024, 64, 1, 64) > L.DECODE_STATIC_SCRATCH_BYTES
+
+
+def test_decode_static_empty_is_a_no_op(L):
+    assert _call_dec_static(L, B=0, q=None, out=None) == L.OK
+    assert _call_dec_static(L, h=0) == L.OK
 
 
 # multi-head: fake addresses 256 MiB apart, never dereferenced
@@ -386,6 +435,8 @@ def test_mha_workspace_size(L):
     (dict(y=0x10000000 + 512), "ERR_ALIAS"),  # y inside xq
     (dict(ws=0x30000000), "ERR_ALIAS"),       # workspace on wk
     (dict(y=0x80000000 + 4096), "ERR_ALIAS"), # y inside the workspace
+    (dict(mask_kind=2, key_lens=0x60000000 + 16), "ERR_ALIAS"),   # y overlaps key_lens
+    (dict(mask_kind=2, key_lens=0x80000000 + 16), "ERR_ALIAS"),   # the workspace overlaps key_lens
     (dict(B=70000, Tq=40000, Tk=40000), "ERR_TOO_LARGE"),   # B T rows past 2^31 - 1
     (dict(Tq=1 << 21, Tk=1 << 21), "ERR_TOO_LARGE"),        # one head's projected rows past 4 GiB
 ])

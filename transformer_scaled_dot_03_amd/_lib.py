@@ -45,6 +45,7 @@ SIGNATURES = {
     "attn_fwd_weights": (_I, [_P] * 6 + [_I] * 6 + [ctypes.c_float, _I, _P, _P]),
     "attn_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, ctypes.c_size_t, _P]),
     "attn_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_decode_static": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P]),
     "attn_status_str": (ctypes.c_char_p, [_I]),
     "attn_last_hip_error": (_I, []),
     "attn_version": (ctypes.c_char_p, []),
@@ -127,6 +128,15 @@ def attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, wo
     """bf16 single-row decode attention over a K/V cache (attn.h `attn_decode`)."""
     return raw_library().attn_decode(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, workspace,
                                      workspace_bytes, stream)
+
+
+def attn_decode_static(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, stream) -> int:
+    """attn_decode with the partials in the library's static device array (attn.h `attn_decode_static`)."""
+    return raw_library().attn_decode_static(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, stream)
+
+
+# bytes of the static device array behind attn_decode_static (attn.h ATTN_DECODE_STATIC_SCRATCH_BYTES)
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 def attn_decode_workspace_bytes(B, h, Tk, d) -> int:

@@ -4,8 +4,10 @@
 // check has passed), choice of the kernel instance and the launch on the
 // caller's stream.  The operation itself is documented in attn.h.
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_launch.h"
@@ -13,6 +15,32 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Device scratch of attn_decode_static: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_err[kMaxDevices];
+
+// the device address of `scratch` on device `dev` (which must be current), or
+// nullptr with the HIP error kept in g_last_hip_error
+void* scratch_on_device(int dev) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && ptr != nullptr) g_scratch[dev].store(ptr, std::memory_order_release);
+    else g_scratch_err[dev].store(e == hipSuccess ? static_cast<int>(hipErrorInvalidSymbol) : static_cast<int>(e),
+                                  std::memory_order_release);
+  });
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) g_last_hip_error = g_scratch_err[dev].load(std::memory_order_acquire);
+  return ptr;
+}
 
 // byte ranges [a, a + na) and [b, b + nb); sizes in 128-bit so no product can wrap
 bool overlaps(const void* a, unsigned __int128 na, const void* b, unsigned __int128 nb) {
@@ -321,9 +349,11 @@ DecodeWorkspace decode_workspace(int B, int h, int Tk, int d) {
   return w;
 }
 
-int decode(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k, int d_v,
-           float scale, int mask_kind, const int32_t* key_lens, void* workspace, size_t workspace_bytes,
-           hipStream_t stream) {
+// Argument checks of the decode entry points, in order, up to (not including)
+// the workspace; `empty` is set for a valid no-op, `ws` to the workspace layout.
+int decode_check(const void* q, const void* k, const void* v, const void* out, int B, int h, int Tk, int d_k,
+                 int d_v, float scale, int mask_kind, const int32_t* key_lens, bool& empty, DecodeWorkspace& ws) {
+  empty = false;
   if (B < 0 || h < 0 || Tk < 0 || d_k < 0 || d_v < 0) return ATTN_ERR_SHAPE;
   if (d_k != d_v) return ATTN_ERR_SHAPE;
   if (d_k != 64 && d_k != 128) return ATTN_ERR_HEADDIM;
@@ -331,28 +361,33 @@ int decode(const void* q, const void* k, const void* v, void* out, int B, int h,
   const bool keypad = (mask_kind & ATTN_MASK_KEYPAD) != 0;
   if (keypad && key_lens == nullptr) return ATTN_ERR_MASK;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-  if (B == 0 || h == 0) return ATTN_OK;
+  if (B == 0 || h == 0) {
+    empty = true;
+    return ATTN_OK;
+  }
   if (q == nullptr || out == nullptr) return ATTN_ERR_NULL;
-  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
   if (Tk > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_NULL;
-  if (misaligned(q, 16) || misaligned(out, 16) || misaligned(workspace, 16) ||
-      (Tk > 0 && (misaligned(k, 16) || misaligned(v, 16))))
+  if (misaligned(q, 16) || misaligned(out, 16) || (Tk > 0 && (misaligned(k, 16) || misaligned(v, 16))))
     return ATTN_ERR_ALIGN;
   if (keypad && misaligned(key_lens, 4)) return ATTN_ERR_ALIGN;
   const int64_t bh = static_cast<int64_t>(B) * h;
   if (static_cast<int64_t>(Tk) * d_k * 2 > 0xffffffffLL) return ATTN_ERR_TOO_LARGE;
-  const DecodeWorkspace ws = decode_workspace(B, h, Tk, d_k);
+  ws = decode_workspace(B, h, Tk, d_k);
   if (bh * ws.n_split > 0x7fffffffLL || bh > 0x7fffffffLL) return ATTN_ERR_TOO_LARGE;
-  if (workspace_bytes < ws.bytes) return ATTN_ERR_WORKSPACE;
-
   typedef unsigned __int128 u128;
-  const u128 nq = (u128)bh * d_k * 2, nkv = (u128)bh * Tk * d_k * 2, nw = ws.bytes;
+  const u128 nq = (u128)bh * d_k * 2, nkv = (u128)bh * Tk * d_k * 2;
   const u128 nkl = keypad ? (u128)B * 4 : 0;
   if (overlaps(out, nq, q, nq) || overlaps(out, nq, k, nkv) || overlaps(out, nq, v, nkv) ||
-      overlaps(out, nq, key_lens, nkl) || overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) ||
-      overlaps(workspace, nw, v, nkv) || overlaps(workspace, nw, out, nq) || overlaps(workspace, nw, key_lens, nkl))
+      overlaps(out, nq, key_lens, nkl))
     return ATTN_ERR_ALIAS;
+  return ATTN_OK;
+}
 
+// enqueues the split and merge kernels with the partials in `workspace` (laid out as `ws`)
+int decode_launch(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k,
+                  float scale, int mask_kind, const int32_t* key_lens, void* workspace, const DecodeWorkspace& ws,
+                  hipStream_t stream) {
+  const bool keypad = (mask_kind & ATTN_MASK_KEYPAD) != 0;
   attn::DecParams p;
   p.q = q;
   p.k = k;
@@ -376,6 +411,50 @@ int decode(const void* q, const void* k, const void* v, void* out, int B, int h,
   return ATTN_OK;
 }
 
+int decode(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k, int d_v,
+           float scale, int mask_kind, const int32_t* key_lens, void* workspace, size_t workspace_bytes,
+           hipStream_t stream) {
+  bool empty = false;
+  DecodeWorkspace ws{};
+  const int st = decode_check(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, empty, ws);
+  if (st != ATTN_OK || empty) return st;
+  if (workspace == nullptr) return ATTN_ERR_WORKSPACE;
+  if (misaligned(workspace, 16)) return ATTN_ERR_ALIGN;
+  if (workspace_bytes < ws.bytes) return ATTN_ERR_WORKSPACE;
+  typedef unsigned __int128 u128;
+  const int64_t bh = static_cast<int64_t>(B) * h;
+  const u128 nq = (u128)bh * d_k * 2, nkv = (u128)bh * Tk * d_k * 2, nw = ws.bytes;
+  const u128 nkl = (mask_kind & ATTN_MASK_KEYPAD) ? (u128)B * 4 : 0;
+  if (overlaps(workspace, nw, q, nq) || overlaps(workspace, nw, k, nkv) || overlaps(workspace, nw, v, nkv) ||
+      overlaps(workspace, nw, out, nq) || overlaps(workspace, nw, key_lens, nkl))
+    return ATTN_ERR_ALIAS;
+  return decode_launch(q, k, v, out, B, h, Tk, d_k, scale, mask_kind, key_lens, workspace, ws, stream);
+}
+
+int decode_static(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k,
+                  int d_v, float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
+  bool empty = false;
+  DecodeWorkspace ws{};
+  const int st = decode_check(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, empty, ws);
+  if (st != ATTN_OK || empty) return st;
+  if (ws.bytes > ATTN_DECODE_STATIC_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  // the array is the current device's: the stream must run there
+  int dev = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) {
+    if (stream == nullptr) sdev = dev;   // the null stream runs on the current device
+    else e = hipStreamGetDevice(stream, &sdev);
+  }
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices || sdev != dev)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int>(e);
+    return ATTN_ERR_HIP;
+  }
+  void* ws_ptr = scratch_on_device(dev);
+  if (ws_ptr == nullptr) return ATTN_ERR_HIP;
+  return decode_launch(q, k, v, out, B, h, Tk, d_k, scale, mask_kind, key_lens, ws_ptr, ws, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,6 +475,11 @@ int attn_fwd_weights(const void* q, const void* k, const void* v, void* out, flo
                      int h, int Tq, int Tk, int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lens,
                      hipStream_t stream) {
   return fwd_weights(q, k, v, out, lse, weights, B, h, Tq, Tk, d_k, d_v, scale, mask_kind, key_lens, stream);
+}
+
+int attn_decode_static(const void* q, const void* k, const void* v, void* out, int B, int h, int Tk, int d_k,
+                       int d_v, float scale, int mask_kind, const int32_t* key_lens, hipStream_t stream) {
+  return decode_static(q, k, v, out, B, h, Tk, d_k, d_v, scale, mask_kind, key_lens, stream);
 }
 
 size_t attn_decode_workspace_bytes(int B, int h, int Tk, int d) {
@@ -449,7 +533,8 @@ const char* attn_status_str(int status) {
     case ATTN_ERR_ALIGN: return "misaligned pointer (bf16/fp32 tensors need 16 bytes; key_lens, lse, delta 4)";
     case ATTN_ERR_SCALE: return "scale is not finite";
     case ATTN_ERR_WORKSPACE:
-      return "workspace missing or smaller than attn_decode_workspace_bytes() / attn_mha_workspace_bytes()";
+      return "workspace missing or smaller than attn_decode_workspace_bytes() / attn_mha_workspace_bytes(), "
+             "or (attn_decode_static) larger than ATTN_DECODE_STATIC_SCRATCH_BYTES";
     case ATTN_ERR_TOO_LARGE: return "too large: over 2^31-1 work-groups, or one head's rows of a tensor over 4 GiB";
     case ATTN_ERR_HIP: return "HIP kernel launch failed (see attn_last_hip_error)";
     default: return "unknown status";
