@@ -44,7 +44,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
 #include <type_traits>
 
 #include "attn_device.h"
@@ -80,7 +79,7 @@ struct Bf16Shape<128> {
 
 template <int D, bool CAUSAL, bool KEYPAD>
 __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves) void attn_fwd_bf16_kernel(
-    Params p_arg) {
+    Params p) {
   constexpr int WAVES = Bf16Shape<D>::kWaves;
   constexpr int RG = Bf16Shape<D>::kRG;      // 32-row groups per wave
   constexpr int BN = Bf16Shape<D>::kBN;      // keys per tile
@@ -112,414 +111,356 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
     else return vb1;
   };
 
-  // ---- persistent schedule: the grid holds at most as many work-groups as
-  // are resident at once, and each takes work units (b, head, query tile) in
-  // turn.  Units are dealt to the 8 XCDs (the hardware hands work-group ids to
-  // the XCDs in turn: id % 8 is the XCD): without masks in contiguous ranges,
-  // so one head's query tiles share one XCD's L2; with a causal or key-padding
-  // mask in order of decreasing work, round robin, which balances the XCDs and
-  // keeps one head's tiles on one XCD when the head count is a multiple of 8.
-  // Within an XCD, work-group k takes list positions k, 2 gx - 1 - k, 2 gx + k,
-  // ... (a snake: the work-group with the shortest first unit takes the
-  // longest second one).
-  const int G = gridDim.x;
-  const int n_units = p_arg.n_wg;
-  const int nbh = p_arg.B * p_arg.H;
-  const int xcd = blockIdx.x % kXcds;
-  const int kx = blockIdx.x / kXcds;
-  const int gx = (G - xcd + kXcds - 1) / kXcds;   // work-groups on this XCD
-  int nx, ustart = 0;                             // units on this XCD, first unit (contiguous ranges)
-  if (CAUSAL || KEYPAD) {
-    nx = n_units > xcd ? (n_units - xcd + kXcds - 1) / kXcds : 0;
+  // ---- work-group -> unit (b, head, query tile).  The hardware hands
+  // work-group ids to the 8 XCDs in turn (id % 8 is the XCD) and, within an
+  // XCD, starts them in id order as earlier ones finish.  Without a mask
+  // every unit is equal and each XCD gets a contiguous range of ids, so one
+  // head's query tiles share its L2.  With a mask the id is read as a rank:
+  //   causal: query tiles from the last (longest) down, then (b, head), so
+  //     the short tiles fill the tail and, with B h a multiple of 8, a head's
+  //     tiles share one XCD;
+  //   key padding: (b, query tile, head), so every batch entry's lengths are
+  //     spread over all XCDs (head h on XCD h % 8 when h is a multiple of 8)
+  //     instead of a contiguous range of batch entries landing on one XCD.
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c = lane & 31;
+  int bh, qt;
+  if (CAUSAL) {
+    const int nbh = p.B * p.H;
+    const int qd = blockIdx.x / nbh;
+    bh = blockIdx.x - qd * nbh;
+    qt = p.n_qtiles - 1 - qd;
+  } else if (KEYPAD) {
+    const int t = blockIdx.x / p.H;
+    const int head_r = blockIdx.x - t * p.H;
+    const int b_r = t / p.n_qtiles;
+    qt = t - b_r * p.n_qtiles;
+    bh = b_r * p.H + head_r;
   } else {
-    const int per = n_units / kXcds, rem = n_units % kXcds;
-    nx = per + (xcd < rem ? 1 : 0);
-    ustart = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  }
-  // key padding with B <= 64 and more units than work-groups: lane b holds the
-  // rank of batch entry b by valid length (longest first, ties by index),
-  // lanes >= B hold B; otherwise batch entries keep their order (with one unit
-  // per work-group the order does not matter, and the lengths are not read)
-  const bool sort_lens = KEYPAD && !CAUSAL && p_arg.B <= 64 && n_units > G;
-  int len_rank = threadIdx.x & 63;
-  if (sort_lens) {
-    const int me = threadIdx.x & 63;
-    const int l_me = me < p_arg.B ? clamp_len(p_arg.key_lens, me, p_arg.Tk) : -1;
-    int rank = 0;
-    for (int j = 0; j < p_arg.B; ++j) {
-      const int l_j = __builtin_amdgcn_readlane(l_me, j);
-      rank += (l_j > l_me || (l_j == l_me && j < me)) ? 1 : 0;
-    }
-    len_rank = rank;
+    tile_of_block(p.n_qtiles, false, bh, qt);
   }
 
-  for (int rnd = 0;; ++rnd) {
-    const int jpos = rnd * gx + ((rnd & 1) ? gx - 1 - kx : kx);
-    if (jpos >= nx) break;
-    // the scalar arguments are re-read from the kernel-argument segment for
-    // every unit (scalar loads): kept in scalar registers across the unit loop
-    // they would not fit beside the tile loop's own (spills to vector lanes).
-    // The pointers stay as they are (kernel-argument pointers are known to
-    // address global memory).
-    typedef __attribute__((address_space(4))) const uint32_t* KernargWords;
-    KernargWords kw = (KernargWords)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(kw));
-    constexpr int kScalarWords = (int)((sizeof(Params) - kParamsScalarOffset) / 4);
-    uint32_t sw[kScalarWords];
+  const int b = bh / p.H;
+  const int Tq = p.Tq, Tk = p.Tk;
+  const int q0 = qt * BM;
+  const int qw = q0 + 32 * RG * w;     // first row of this wave; group r holds rows qw + 32r + c
+
+  int kend = Tk;                       // keys [0, kend) hold data
+  if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
+  int kend_wg = kend;
+  if (CAUSAL) kend_wg = min(kend_wg, q0 + BM);
+  const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
+  int kend_w = CAUSAL ? min(kend, qw + 32 * RG) : kend;
+  if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
+  const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
+
+  // tensors addressed through (batch, head, row) strides; rows are d contiguous elements
+  const int head = bh - b * p.H;
+  const __bf16* Qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + head * p.q_sh;
+  const __bf16* Kg = static_cast<const __bf16*>(p.k) + b * p.k_sb + head * p.k_sh;
+  const __bf16* Vg = static_cast<const __bf16*>(p.v) + b * p.v_sb + head * p.v_sh;
+  __bf16* Og = static_cast<__bf16*>(p.o) + b * p.o_sb + head * p.o_sh;
+  const uint32_t krs = 2u * p.k_sr, vrs = 2u * p.v_sr;    // row strides in bytes
+
+  // Q rows -> registers (B operand of S^T); d index of step t is 16t + 8g + e.
+  bf16x8 qf[RG][DT];
 #pragma unroll
-    for (int i = 0; i < kScalarWords; ++i) sw[i] = kw[kParamsScalarOffset / 4 + i];
-    Params p = p_arg;
-    __builtin_memcpy(reinterpret_cast<char*>(&p) + kParamsScalarOffset, sw, sizeof(sw));
-    int bh, qt;
-    if (CAUSAL) {
-      // rank r: query tiles from the last (longest) down, then (b, head)
-      const int r = jpos * kXcds + xcd;
-      const int qd = r / nbh;
-      bh = r - qd * nbh;
-      qt = p.n_qtiles - 1 - qd;
-    } else if (KEYPAD) {
-      // rank r: batch entries by decreasing length, then query tile, then head
-      const int r = jpos * kXcds + xcd;
-      const int t = r / p.H;
-      const int head_r = r - t * p.H;
-      const int lr = t / p.n_qtiles;
-      qt = t - lr * p.n_qtiles;
-      const int b_r = sort_lens ? (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(len_rank == lr)) : lr;
-      bh = b_r * p.H + head_r;
-    } else {
-      const int u = ustart + jpos;
-      bh = u / p.n_qtiles;
-      qt = u - bh * p.n_qtiles;
+  for (int r = 0; r < RG; ++r) {
+    const int row = qw + 32 * r + c;
+    const bool ok = row < Tq;
+    const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * p.q_sr + 8 * g;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) {
+      u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+      if (p.neg) x ^= 0x80008000u;     // negative scale: use -Q and |scale| (exact)
+      qf[r][t] = __builtin_bit_cast(bf16x8, x);
     }
-    // lane constants are derived inside the unit loop from an opaque copy of
-    // the thread id: hoisted above the loop they would stay live across it
-    // and crowd out the registers the pinned tile schedule needs
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    const int lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = lane >> 5, c = lane & 31;
+  }
 
-    const int b = bh / p.H;
-    const int Tq = p.Tq, Tk = p.Tk;
-    const int q0 = qt * BM;
-    const int qw = q0 + 32 * RG * w;     // first row of this wave; group r holds rows qw + 32r + c
-
-    int kend = Tk;                       // keys [0, kend) hold data
-    if (KEYPAD) kend = min(kend, clamp_len(p.key_lens, b, Tk));
-    int kend_wg = kend;
-    if (CAUSAL) kend_wg = min(kend_wg, q0 + BM);
-    const int ntiles = kend_wg > 0 ? (kend_wg + BN - 1) / BN : 0;
-    int kend_w = CAUSAL ? min(kend, qw + 32 * RG) : kend;
-    if (qw >= Tq) kend_w = 0;            // wave entirely past the last row
-    const int ntw = kend_w > 0 ? (kend_w + BN - 1) / BN : 0;
-
-    // tensors addressed through (batch, head, row) strides; rows are d contiguous elements
-    const int head = bh - b * p.H;
-    const __bf16* Qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + head * p.q_sh;
-    const __bf16* Kg = static_cast<const __bf16*>(p.k) + b * p.k_sb + head * p.k_sh;
-    const __bf16* Vg = static_cast<const __bf16*>(p.v) + b * p.v_sb + head * p.v_sh;
-    __bf16* Og = static_cast<__bf16*>(p.o) + b * p.o_sb + head * p.o_sh;
-    const uint32_t krs = 2u * p.k_sr, vrs = 2u * p.v_sr;    // row strides in bytes
-
-    // Q rows -> registers (B operand of S^T); d index of step t is 16t + 8g + e.
-    bf16x8 qf[RG][DT];
+  // ---- direct-to-LDS staging: this lane's source offsets for its NLD 1 KB blocks
+  uint32_t k_src[NLD], v_src[NLD];
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const int row = qw + 32 * r + c;
-      const bool ok = row < Tq;
-      const __bf16* qp = Qg + (int64_t)(ok ? row : 0) * p.q_sr + 8 * g;
+  for (int u = 0; u < NLD; ++u) {
+    const int pos = (WAVES * u + w) * 1024 + 16 * lane;
+    const int r = pos / ROWB, pc = (pos % ROWB) / 16;
+    const int key = (r & ~31) + sigma32(r & 31);
+    k_src[u] = key * krs + 16 * (pc ^ k_swz<D>(r));
+    v_src[u] = r * vrs + 16 * (pc ^ v_swz<D>(r));
+  }
+  // rows at or past kend read as zero: the range ends with the last valid row's d elements
+  auto load_k = [&](int j0, char* kt) {
+    const __amdgpu_buffer_rsrc_t kr =
+        buffer_rsrc(Kg + (int64_t)j0 * p.k_sr, (uint32_t)(kend - j0 - 1) * krs + ROWB);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) lds_dma16(kr, kt + (WAVES * u + w) * 1024, k_src[u]);
+  };
+  auto load_v = [&](int j0, char* vt) {
+    const __amdgpu_buffer_rsrc_t vr =
+        buffer_rsrc(Vg + (int64_t)j0 * p.v_sr, (uint32_t)(kend - j0 - 1) * vrs + ROWB);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) lds_dma16(vr, vt + (WAVES * u + w) * 1024, v_src[u]);
+  };
+
+  // ---- LDS read offsets (bytes, within a tile)
+  // K: lane (c, g), step t reads logical chunk 2t + g of slot row 32 hh + c
+  int k_rd[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) k_rd[t] = c * ROWB + 16 * ((2 * t + g) ^ k_swz<D>(c));
+  // V^T via transposed reads: in each 16-lane group G (h = G & 1, g = G >> 1)
+  // source lane s reads 4 consecutive output columns of key row
+  // 8g + e0 + s/4 (+ 32 hh + 16 m); output lane j then holds that column of
+  // keys e0 .. e0+3 -- the A operand of O^T = V^T P^T.
+  int v_rd[NO];
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    const int h = G & 1, gg = G >> 1;
+    const int r = 8 * gg + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const int lc = (D / 16) * (sl & 1) + 2 * i + h;
+      v_rd[i] = r * ROWB + 16 * (lc ^ v_swz<D>(r)) + 8 * ((sl >> 1) & 1);
+    }
+  }
+
+  // per-lane state of each row group: output accumulator (O^T, row c,
+  // columns tau), reference maximum (scaled, log2 units), its offset (0 while
+  // no key has been seen), this lane's half of the row sum
+  f32x16 acc[RG][NO];
+  float m_run[RG], base[RG], l_run[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+#pragma unroll
+    for (int i = 0; i < NO; ++i) acc[r][i] = f32x16{};
+    m_run[r] = kNegInf;
+    base[r] = 0.f;
+    l_run[r] = 0.f;
+  }
+  const float cs = p.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // S^T = K Q^T for the BN keys of a K tile: register e of s[r][hh] holds
+  // key 32hh + 16(e/8) + 8g + e%8 of the tile for row qw + 32r + c
+  auto scores = [&](const char* kt, f32x16 (&s)[RG][NH]) {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) s[r][hh] = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        u32x4 x = ok ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
-        if (p.neg) x ^= 0x80008000u;     // negative scale: use -Q and |scale| (exact)
-        qf[r][t] = __builtin_bit_cast(bf16x8, x);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + k_rd[t]);
+#pragma unroll
+        for (int r = 0; r < RG; ++r)
+          s[r][hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][t], s[r][hh], 0, 0, 0);
       }
     }
+  };
 
-    // ---- direct-to-LDS staging: this lane's source offsets for its NLD 1 KB blocks
-    uint32_t k_src[NLD], v_src[NLD];
+  // O^T += V^T P^T over one V tile
+  auto pv = [&](const char* v_cur, const bf16x8 (&pk)[RG][NH][2]) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int pos = (WAVES * u + w) * 1024 + 16 * lane;
-      const int r = pos / ROWB, pc = (pos % ROWB) / 16;
-      const int key = (r & ~31) + sigma32(r & 31);
-      k_src[u] = key * krs + 16 * (pc ^ k_swz<D>(r));
-      v_src[u] = r * vrs + 16 * (pc ^ v_swz<D>(r));
-    }
-    // rows at or past kend read as zero: the range ends with the last valid row's d elements
-    auto load_k = [&](int j0, char* kt) {
-      const __amdgpu_buffer_rsrc_t kr =
-          buffer_rsrc(Kg + (int64_t)j0 * p.k_sr, (uint32_t)(kend - j0 - 1) * krs + ROWB);
+    for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) lds_dma16(kr, kt + (WAVES * u + w) * 1024, k_src[u]);
-    };
-    auto load_v = [&](int j0, char* vt) {
-      const __amdgpu_buffer_rsrc_t vr =
-          buffer_rsrc(Vg + (int64_t)j0 * p.v_sr, (uint32_t)(kend - j0 - 1) * vrs + ROWB);
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int u = 0; u < NLD; ++u) lds_dma16(vr, vt + (WAVES * u + w) * 1024, v_src[u]);
-    };
-
-    // ---- LDS read offsets (bytes, within a tile)
-    // K: lane (c, g), step t reads logical chunk 2t + g of slot row 32 hh + c
-    int k_rd[DT];
-#pragma unroll
-    for (int t = 0; t < DT; ++t) k_rd[t] = c * ROWB + 16 * ((2 * t + g) ^ k_swz<D>(c));
-    // V^T via transposed reads: in each 16-lane group G (h = G & 1, g = G >> 1)
-    // source lane s reads 4 consecutive output columns of key row
-    // 8g + e0 + s/4 (+ 32 hh + 16 m); output lane j then holds that column of
-    // keys e0 .. e0+3 -- the A operand of O^T = V^T P^T.
-    int v_rd[NO];
-    {
-      const int G = lane >> 4, sl = lane & 15;
-      const int h = G & 1, gg = G >> 1;
-      const int r = 8 * gg + (sl >> 2);
-#pragma unroll
-      for (int i = 0; i < NO; ++i) {
-        const int lc = (D / 16) * (sl & 1) + 2 * i + h;
-        v_rd[i] = r * ROWB + 16 * (lc ^ v_swz<D>(r)) + 8 * ((sl >> 1) & 1);
-      }
-    }
-
-    // per-lane state of each row group: output accumulator (O^T, row c,
-    // columns tau), reference maximum (scaled, log2 units), its offset (0 while
-    // no key has been seen), this lane's half of the row sum
-    f32x16 acc[RG][NO];
-    float m_run[RG], base[RG], l_run[RG];
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-#pragma unroll
-      for (int i = 0; i < NO; ++i) acc[r][i] = f32x16{};
-      m_run[r] = kNegInf;
-      base[r] = 0.f;
-      l_run[r] = 0.f;
-    }
-    const float cs = p.scale_log2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-    // S^T = K Q^T for the BN keys of a K tile: register e of s[r][hh] holds
-    // key 32hh + 16(e/8) + 8g + e%8 of the tile for row qw + 32r + c
-    auto scores = [&](const char* kt, f32x16 (&s)[RG][NH]) {
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) s[r][hh] = f32x16{};
-#pragma unroll
-        for (int t = 0; t < DT; ++t) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + 32 * hh * ROWB + k_rd[t]);
+        for (int i = 0; i < NO; ++i) {
+          const char* vb = v_cur + (32 * hh + 16 * m) * ROWB + v_rd[i];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
+          const bf16x8 vf =
+              __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int r = 0; r < RG; ++r)
-            s[r][hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[r][t], s[r][hh], 0, 0, 0);
+            acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[r][hh][m], acc[r][i], 0, 0, 0);
         }
-      }
-    };
+  };
 
-    // O^T += V^T P^T over one V tile
-    auto pv = [&](const char* v_cur, const bf16x8 (&pk)[RG][NH][2]) {
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int i = 0; i < NO; ++i) {
-            const char* vb = v_cur + (32 * hh + 16 * m) * ROWB + v_rd[i];
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 4 * ROWB));
-            const bf16x8 vf =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-            for (int r = 0; r < RG; ++r)
-              acc[r][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pk[r][hh][m], acc[r][i], 0, 0, 0);
-          }
-    };
-
-    {
-      // Step j: O^T += V^T P(j-1)^T on the matrix cores interleaved with the row
-      // maxima of tile j on the vector ALUs; the (rare) rescale; then S(j+1) =
-      // K(j+1) Q^T on the matrix cores interleaved with the exponentials of
-      // tile j.  Step j reads V(j-1) and K(j+1) and loads K(j+2) and V(j).
-      // A wave issues in order and an MFMA waits for the matrix pipe, so
-      // without the pinned interleave the compiler's order (all MFMAs of a
-      // block, then all vector work) leaves one unit idle while the other runs.
-      f32x16 s2[2][RG][NH];
-      bf16x8 pk[RG][NH][2];
-      float m_tile[RG];
-      auto row_max = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) -> bool {
-        if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
-#pragma unroll
-          for (int r = 0; r < RG; ++r)
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) {
-                const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-                bool ok = key < kend;
-                if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
-                sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
-              }
-        }
-        // IEEE maximum (NaN-propagating): gfx950's v_maximum3_f32, with no
-        // canonicalising moves in front of it (a NaN score makes the row NaN
-        // through its exponential either way)
-        auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
-        bool grow = false;
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          float mx[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) mx[k] = sc[r][k / 2][8 * (k % 2)];
-#pragma unroll
-          for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx[(2 * hh + e / 8) % 4] = vmax(mx[(2 * hh + e / 8) % 4], sc[r][hh][e]);
-          const float m4 = vmax(vmax(mx[0], mx[1]), vmax(mx[2], mx[3]));
-          const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4), __float_as_uint(m4), false, false);
-          m_tile[r] = vmax(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * cs;
-          grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
-        }
-        return grow;
-      };
-      auto rescale = [&]() {
-#pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          const float m_new = fmaxf(m_run[r], m_tile[r]);
-          const float b_new = (m_new == kNegInf) ? 0.f : m_new;
-          const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);
-          m_run[r] = m_new;
-          base[r] = b_new;
-          l_run[r] *= alpha;
-#pragma unroll
-          for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
-        }
-      };
-      auto probs = [&](const f32x16 (&sc)[RG][NH]) {
+  {
+    // Step j: O^T += V^T P(j-1)^T on the matrix cores interleaved with the row
+    // maxima of tile j on the vector ALUs; the (rare) rescale; then S(j+1) =
+    // K(j+1) Q^T on the matrix cores interleaved with the exponentials of
+    // tile j.  Step j reads V(j-1) and K(j+1) and loads K(j+2) and V(j).
+    // A wave issues in order and an MFMA waits for the matrix pipe, so
+    // without the pinned interleave the compiler's order (all MFMAs of a
+    // block, then all vector work) leaves one unit idle while the other runs.
+    f32x16 s2[2][RG][NH];
+    bf16x8 pk[RG][NH][2];
+    float m_tile[RG];
+    auto row_max = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) -> bool {
+      if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
 #pragma unroll
         for (int r = 0; r < RG; ++r)
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              f32x8 e8;
-#pragma unroll
-              for (int j = 0; j < 8; ++j)
-                e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
-              pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
-                l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
-              }
+            for (int e = 0; e < 16; ++e) {
+              const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
+              bool ok = key < kend;
+              if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
+              sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
             }
-      };
-      constexpr int NPV = NH * 2 * NO * RG;   // P V^T operations, 2 LDS reads each
-      constexpr int NS = NH * DT * RG;        // score operations, 1 LDS read each
-      // block A order: 8 reads, then per operation: 1 MFMA, 2 VALU, 2 reads
-      auto pin_a = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
-        static_for<0, NPV>([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
-          __builtin_amdgcn_sched_group_barrier(0x402, 2, 2);
-          if constexpr (i + 4 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
-        });
-      };
-      // block C order: 4 reads, then per operation: 1 MFMA, 7 VALU, 1 read
-      auto pin_c = [&]() {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
-        static_for<0, NS>([&](auto I) {
-          constexpr int i = decltype(I)::value;
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-          __builtin_amdgcn_sched_group_barrier(0x402, 6, 3);
-          if constexpr (i + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
-        });
-      };
-      // the probabilities and row sums stay in the step that computes them (the
-      // compiler would otherwise sink them past the barrier into the next step)
-      auto pin_p = [&]() {
+      }
+      // IEEE maximum (NaN-propagating): gfx950's v_maximum3_f32, with no
+      // canonicalising moves in front of it (a NaN score makes the row NaN
+      // through its exponential either way)
+      auto vmax = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+      bool grow = false;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
+      for (int r = 0; r < RG; ++r) {
+        float mx[4];
 #pragma unroll
-          for (int hh = 0; hh < NH; ++hh)
+        for (int k = 0; k < 4; ++k) mx[k] = sc[r][k / 2][8 * (k % 2)];
 #pragma unroll
-            for (int m = 0; m < 2; ++m) asm volatile("" ::"v"(pk[r][hh][m]));
-          asm volatile("" ::"v"(l_run[r]));
-        }
-      };
-      // it: step index; U: it % 2 (buffer parity)
-      auto step = [&](int it, auto U, auto MASKED) {
-        constexpr int u = decltype(U)::value;
-        f32x16 (&sc)[RG][NH] = s2[u];
-        f32x16 (&sn)[RG][NH] = s2[u ^ 1];
-        const int j0 = it * BN;
-        if (it + 2 < ntiles) load_k(j0 + 2 * BN, kbuf(std::integral_constant<int, u>{}));
-        if (it < ntiles) load_v(j0, vbuf(std::integral_constant<int, u>{}));
-        if constexpr (!decltype(MASKED)::value) {
-          pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx[(2 * hh + e / 8) % 4] = vmax(mx[(2 * hh + e / 8) % 4], sc[r][hh][e]);
+        const float m4 = vmax(vmax(mx[0], mx[1]), vmax(mx[2], mx[3]));
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4), __float_as_uint(m4), false, false);
+        m_tile[r] = vmax(__uint_as_float(pr[0]), __uint_as_float(pr[1])) * cs;
+        grow = grow || (m_tile[r] > m_run[r] + kRescaleThreshold);
+      }
+      return grow;
+    };
+    auto rescale = [&]() {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        const float m_new = fmaxf(m_run[r], m_tile[r]);
+        const float b_new = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[r] - b_new);
+        m_run[r] = m_new;
+        base[r] = b_new;
+        l_run[r] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NO; ++i) acc[r][i] *= alpha;
+      }
+    };
+    auto probs = [&](const f32x16 (&sc)[RG][NH]) {
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            f32x8 e8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              e8[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r][hh][8 * m + j], cs, -base[r]));
+            pk[r][hh][m] = __builtin_convertvector(e8, bf16x8);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x2 pr2 = {pk[r][hh][m][2 * j], pk[r][hh][m][2 * j + 1]};
+              l_run[r] = __builtin_amdgcn_fdot2_f32_bf16(pr2, ones, l_run[r], false);
+            }
+          }
+    };
+    constexpr int NPV = NH * 2 * NO * RG;   // P V^T operations, 2 LDS reads each
+    constexpr int NS = NH * DT * RG;        // score operations, 1 LDS read each
+    // block A order: 8 reads, then per operation: 1 MFMA, 2 VALU, 2 reads
+    auto pin_a = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+      static_for<0, NPV>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        __builtin_amdgcn_sched_group_barrier(0x402, 2, 2);
+        if constexpr (i + 4 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+      });
+    };
+    // block C order: 4 reads, then per operation: 1 MFMA, 7 VALU, 1 read
+    auto pin_c = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 3);
+      static_for<0, NS>([&](auto I) {
+        constexpr int i = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        __builtin_amdgcn_sched_group_barrier(0x402, 6, 3);
+        if constexpr (i + 4 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
+      });
+    };
+    // the probabilities and row sums stay in the step that computes them (the
+    // compiler would otherwise sink them past the barrier into the next step)
+    auto pin_p = [&]() {
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) asm volatile("" ::"v"(pk[r][hh][m]));
+        asm volatile("" ::"v"(l_run[r]));
+      }
+    };
+    // it: step index; U: it % 2 (buffer parity)
+    auto step = [&](int it, auto U, auto MASKED) {
+      constexpr int u = decltype(U)::value;
+      f32x16 (&sc)[RG][NH] = s2[u];
+      f32x16 (&sn)[RG][NH] = s2[u ^ 1];
+      const int j0 = it * BN;
+      if (it + 2 < ntiles) load_k(j0 + 2 * BN, kbuf(std::integral_constant<int, u>{}));
+      if (it < ntiles) load_v(j0, vbuf(std::integral_constant<int, u>{}));
+      if constexpr (!decltype(MASKED)::value) {
+        pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
+        const bool grow = row_max(j0, sc, MASKED);
+        pin_a();
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
+        scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+        probs(sc);
+        pin_c();
+        pin_p();
+      } else {
+        if (it >= 1 && it - 1 < ntw) pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
+        if (it < ntw) {
           const bool grow = row_max(j0, sc, MASKED);
-          pin_a();
           if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
-          scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
+          if (it + 1 < ntw) scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
           probs(sc);
-          pin_c();
           pin_p();
-        } else {
-          if (it >= 1 && it - 1 < ntw) pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
-          if (it < ntw) {
-            const bool grow = row_max(j0, sc, MASKED);
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) rescale();
-            if (it + 1 < ntw) scores(kbuf(std::integral_constant<int, u + 1>{}), sn);
-            probs(sc);
-            pin_p();
-          }
         }
-        pipeline_barrier<0>();
-      };
+      }
+      pipeline_barrier<0>();
+    };
 
-      // prologue: K(0), K(1); the scores of tile 0; K(0) consumed before step 0 reloads its buffer
-      if (ntiles > 0) load_k(0, kb0);
-      if (ntiles > 1) load_k(BN, kb1);
-      pipeline_barrier<0>();
-      if (ntw > 0) scores(kb0, s2[0]);
-      pipeline_barrier<0>();
-      // tiles [0, nint) hold no masked key for any row of the work-group
-      int nint = kend / BN;
-      if (CAUSAL) nint = min(nint, (q0 + 1) / BN);
-      nint = min(nint, ntiles);
-      // steps 0 .. ntiles; step 0 (no P V^T yet) and steps >= nint take the general path
-      step(0, std::integral_constant<int, 0>{}, std::true_type{});
-      int it0 = 1;
-      for (; it0 + 1 < nint; it0 += 2) {
-        step(it0, std::integral_constant<int, 1>{}, std::false_type{});
-        step(it0 + 1, std::integral_constant<int, 0>{}, std::false_type{});
-      }
-      for (; it0 <= ntiles; it0 += 2) {
-        step(it0, std::integral_constant<int, 1>{}, std::true_type{});
-        if (it0 + 1 <= ntiles) step(it0 + 1, std::integral_constant<int, 0>{}, std::true_type{});
-      }
+    // prologue: K(0), K(1); the scores of tile 0; K(0) consumed before step 0 reloads its buffer
+    if (ntiles > 0) load_k(0, kb0);
+    if (ntiles > 1) load_k(BN, kb1);
+    pipeline_barrier<0>();
+    if (ntw > 0) scores(kb0, s2[0]);
+    pipeline_barrier<0>();
+    // tiles [0, nint) hold no masked key for any row of the work-group
+    int nint = kend / BN;
+    if (CAUSAL) nint = min(nint, (q0 + 1) / BN);
+    nint = min(nint, ntiles);
+    // steps 0 .. ntiles; step 0 (no P V^T yet) and steps >= nint take the general path
+    step(0, std::integral_constant<int, 0>{}, std::true_type{});
+    int it0 = 1;
+    for (; it0 + 1 < nint; it0 += 2) {
+      step(it0, std::integral_constant<int, 1>{}, std::false_type{});
+      step(it0 + 1, std::integral_constant<int, 0>{}, std::false_type{});
     }
+    for (; it0 <= ntiles; it0 += 2) {
+      step(it0, std::integral_constant<int, 1>{}, std::true_type{});
+      if (it0 + 1 <= ntiles) step(it0 + 1, std::integral_constant<int, 0>{}, std::true_type{});
+    }
+  }
 
-    // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane;
-    // optionally the row's log-sum-exp: ln 2 * (base + log2 l), -inf if no key ----
+  // ---- epilogue: O = O / l, one rounding to bf16, D contiguous bytes per lane;
+  // optionally the row's log-sum-exp: ln 2 * (base + log2 l), -inf if no key ----
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const int row = qw + 32 * r + c;
-      const float l_tot = pair_sum(l_run[r]);
-      if (p.lse != nullptr && g == 0 && row < Tq)
-        p.lse[(int64_t)bh * Tq + row] =
-            l_tot > 0.f ? 0.69314718055994531f * (base[r] + __builtin_log2f(l_tot)) : kNegInf;
-      if (row < Tq) {
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        __bf16* op = Og + (int64_t)row * p.o_sr + (D / 2) * g;
+  for (int r = 0; r < RG; ++r) {
+    const int row = qw + 32 * r + c;
+    const float l_tot = pair_sum(l_run[r]);
+    if (p.lse != nullptr && g == 0 && row < Tq)
+      p.lse[(int64_t)bh * Tq + row] =
+          l_tot > 0.f ? 0.69314718055994531f * (base[r] + __builtin_log2f(l_tot)) : kNegInf;
+    if (row < Tq) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      __bf16* op = Og + (int64_t)row * p.o_sr + (D / 2) * g;
 #pragma unroll
-        for (int i = 0; i < NO; ++i) {
+      for (int i = 0; i < NO; ++i) {
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            f32x8 o8;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          f32x8 o8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o8[j] = acc[r][i][8 * h2 + j] * inv;
-            *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
-          }
+          for (int j = 0; j < 8; ++j) o8[j] = acc[r][i][8 * h2 + j] * inv;
+          *reinterpret_cast<bf16x8*>(op + 16 * i + 8 * h2) = __builtin_convertvector(o8, bf16x8);
         }
       }
     }
@@ -725,40 +666,12 @@ int rows_per_block(DType dt, int d) {
                   : 32 * Bf16Shape<64>::kRG * Bf16Shape<64>::kWaves;
 }
 
-// Work-groups of the bf16 kernel instance `slot` resident on the current
-// device at once (resident per CU x CUs), cached per device; 0 if unknown.
-static int resident_groups(int slot, const void* fn, int threads) {
-  constexpr int kMaxDev = 64, kSlots = 8;
-  static std::atomic<int> cache[kMaxDev][kSlots];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev || slot < 0 || slot >= kSlots) return 0;
-  int n = cache[dev][slot].load(std::memory_order_relaxed);
-  if (n == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    n = per_cu * cus;
-    if (n <= 0) return 0;
-    cache[dev][slot].store(n, std::memory_order_relaxed);   // every thread stores the same value
-  }
-  return n;
-}
-
 hipError_t launch_fwd(const Params& prm, DType dt, int d, bool causal, bool keypad, hipStream_t stream) {
   const void* fn = (d == 64) ? pick<64>(dt == DType::F32, causal, keypad)
                              : pick<128>(dt == DType::F32, causal, keypad);
   Params local = prm;
   void* args[] = {&local};
-  const int threads = threads_per_block(dt, d);
-  int grid = prm.n_wg;
-  if (dt == DType::BF16) {
-    // persistent: no more work-groups than are resident at once (each loops
-    // over units); a multiple of the 8 XCDs, so every XCD's units have takers
-    const int slot = (d == 128 ? 4 : 0) + (causal ? 2 : 0) + (keypad ? 1 : 0);
-    const int resident = resident_groups(slot, fn, threads) / kXcds * kXcds;
-    if (resident >= kXcds && resident < grid) grid = resident;
-  }
-  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, stream);
+  return hipLaunchKernel(fn, dim3(prm.n_wg), dim3(threads_per_block(dt, d)), args, 0, stream);
 }
 
 }  // namespace attn

@@ -4,7 +4,6 @@
 #define ATTN_LAUNCH_H_
 
 #include <hip/hip_runtime.h>
-#include <stddef.h>
 #include <stdint.h>
 
 namespace attn {
@@ -13,8 +12,6 @@ enum class DType { BF16, F32 };
 
 // Kernel arguments, passed by value.  Tensors are dense row-major
 // [B, H, T, d]; the kernel derives every offset in 64-bit arithmetic.
-// Pointers first, then every scalar: the bf16 kernel re-reads the scalar
-// tail (from `B` on) from the kernel-argument segment once per work unit.
 struct Params {
   const void* q;
   const void* k;
@@ -26,16 +23,13 @@ struct Params {
   float scale_log2;         // |scale| * log2(e): scores feed exp2
   int neg;                  // 1 when scale < 0: the kernel negates Q (exact)
   int n_qtiles;             // ceil(Tq / rows_per_block(dt, d))
-  int n_wg;                 // B * H * n_qtiles work units (work-groups unless the grid is persistent)
+  int n_wg;                 // B * H * n_qtiles work-groups
   // Element strides of batch entry, head and row for each tensor (the bf16
   // kernel honours them; the dense [B, H, T, d] layout has row = d, head = T d,
   // batch = H T d, and is what the fp32 kernel assumes).
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_sr, k_sr, v_sr, o_sr;
 };
-constexpr size_t kParamsScalarOffset = offsetof(Params, B);
-static_assert(kParamsScalarOffset % 4 == 0 && sizeof(Params) % 4 == 0, "scalar tail in whole words");
-
 // fills the strides of the dense [B, H, T, d] layout
 inline void set_dense_strides(Params& p, int d) {
   p.q_sr = p.k_sr = p.v_sr = p.o_sr = d;
