@@ -27,7 +27,11 @@ LINK: dict[str, list[str]] = {}
 # measurement aid for the benchmark: pure matrix-core loop (include/mfma_probe.h)
 PROBE_LIB_PATH = os.path.join(PKG, "libmfma_probe.so")
 PROBE_SOURCES = ["mfma_probe.hip"]
+# test-only copy of the library whose forward waits for every K/V tile load
+# before reading LDS (no load overlaps compute): the race check of the staging
+SERIAL_TEST_LIB_PATH = os.path.join(PKG, "libattn_serial_test.so")
 TARGETS = [(LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)]
+TEST_TARGETS = [(SERIAL_TEST_LIB_PATH, SOURCES, ["-DATTN_FWD_TEST_SERIAL_STAGING=1"])]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code (kept out on
@@ -46,10 +50,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: ROCm is required to build libattn.so")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every library (always recompiles); return the attention library's path."""
+def build(verbose: bool = False, extra_flags: list[str] | None = None, tests: bool = True) -> str:
+    """Compile every library (always recompiles), and the test-only libraries
+    unless tests=False; return the attention library's path."""
     for path, sources in TARGETS:
         _build_one(path, sources, verbose, extra_flags)
+    if tests:
+        for path, sources, flags in TEST_TARGETS:
+            _build_one(path, sources, verbose, [*(extra_flags or []), *flags])
     return LIB_PATH
 
 

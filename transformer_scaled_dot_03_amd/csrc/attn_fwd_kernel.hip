@@ -49,7 +49,18 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+// A test-only build (-DATTN_FWD_TEST_SERIAL_STAGING=1, built as
+// libattn_serial_test.so, never as libattn.so) waits for each step's K/V loads
+// before the step reads LDS: no load is in flight while any wave reads a tile,
+// so the staging cannot race; its outputs must equal the pipelined kernel's
+// bit for bit.
+#ifndef ATTN_FWD_TEST_SERIAL_STAGING
+#define ATTN_FWD_TEST_SERIAL_STAGING 0
+#endif
+
 namespace attn {
+
+constexpr bool kSerialStaging = ATTN_FWD_TEST_SERIAL_STAGING != 0;
 
 // ---------------------------------------------------------------------------
 // bf16 kernel
@@ -116,9 +127,10 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
   // XCD, starts them in id order as earlier ones finish.  Without a mask
   // every unit is equal and each XCD gets a contiguous range of ids, so one
   // head's query tiles share its L2.  With a mask the id is read as a rank:
-  //   causal: query tiles from the last (longest) down, then (b, head), so
-  //     the short tiles fill the tail and, with B h a multiple of 8, a head's
-  //     tiles share one XCD;
+  //   causal: XCD x takes the heads x, x + 8, ... in groups of up to 16, and
+  //     within a group the query tiles from the last (longest) down, so the
+  //     short tiles fill the gaps and the tail while a group's keys and values
+  //     stay in the XCD's L2 (B h not a multiple of 8: all heads form one group);
   //   key padding: (b, query tile, head), so every batch entry's lengths are
   //     spread over all XCDs (head h on XCD h % 8 when h is a multiple of 8)
   //     instead of a contiguous range of batch entries landing on one XCD.
@@ -129,8 +141,19 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
   int bh, qt;
   if (CAUSAL) {
     const int nbh = p.B * p.H;
-    const int qd = blockIdx.x / nbh;
-    bh = blockIdx.x - qd * nbh;
+    int qd;
+    if (nbh % kXcds == 0) {
+      const int per_xcd = nbh / kXcds;
+      int hg = 16;                        // heads per group: a power of two dividing per_xcd
+      while (per_xcd % hg != 0) hg >>= 1;
+      const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+      const int grp = j / (hg * p.n_qtiles), k = j - grp * (hg * p.n_qtiles);
+      qd = k / hg;
+      bh = x + kXcds * (grp * hg + (k - qd * hg));
+    } else {
+      qd = blockIdx.x / nbh;
+      bh = blockIdx.x - qd * nbh;
+    }
     qt = p.n_qtiles - 1 - qd;
   } else if (KEYPAD) {
     const int t = blockIdx.x / p.H;
@@ -284,8 +307,21 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
     // A wave issues in order and an MFMA waits for the matrix pipe, so
     // without the pinned interleave the compiler's order (all MFMAs of a
     // block, then all vector work) leaves one unit idle while the other runs.
+    // zero-initialised: waves whose rows all lie past Tq (ragged last query
+    // tile) still run the interior steps with the rest of the work-group;
+    // their results are never stored, but they compute on defined values
     f32x16 s2[2][RG][NH];
     bf16x8 pk[RG][NH][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < RG; ++r)
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) s2[u][r][hh] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < RG; ++r)
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) pk[r][hh][0] = pk[r][hh][1] = bf16x8{};
     float m_tile[RG];
     auto row_max = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) -> bool {
       if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
@@ -396,6 +432,8 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
       const int j0 = it * BN;
       if (it + 2 < ntiles) load_k(j0 + 2 * BN, kbuf(std::integral_constant<int, u>{}));
       if (it < ntiles) load_v(j0, vbuf(std::integral_constant<int, u>{}));
+      // test build only: the step's loads land before any of its LDS reads
+      if constexpr (kSerialStaging) pipeline_barrier<0>();
       if constexpr (!decltype(MASKED)::value) {
         pv(vbuf(std::integral_constant<int, u + 1>{}), pk);
         const bool grow = row_max(j0, sc, MASKED);
