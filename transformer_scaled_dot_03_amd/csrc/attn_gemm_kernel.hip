@@ -243,12 +243,14 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void attn_gemm_bf16_kernel(Gemm
   }
 }
 
-// compute units of the current device (the persistent grid size), cached per device
-static int device_cus() {
+// compute units of the device `stream` runs on (the persistent grid size),
+// cached per device; the null stream runs on the current device
+static int device_cus(hipStream_t stream) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cus[kMaxDev];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  const hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
   int n = cus[dev].load(std::memory_order_relaxed);
   if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -273,7 +275,7 @@ hipError_t launch_gemm(const GemmParams& p0, hipStream_t stream) {
   p.n_mt = static_cast<int>(n_mt);
   // one work-group per tile, or one per CU (a multiple of the 8 XCDs) looping over tiles
   int64_t grid = ntile;
-  const int cus = device_cus() / kXcds * kXcds;
+  const int cus = device_cus(stream) / kXcds * kXcds;
   if (cus >= kXcds && ntile > cus) grid = cus;
   void* args[] = {&p};
   return hipLaunchKernel(reinterpret_cast<const void*>(&attn_gemm_bf16_kernel), dim3(static_cast<unsigned>(grid)),
