@@ -121,17 +121,222 @@ def mfma_ceiling(torch, dev, blocks=512, iters=5000, reps=3):
     return best
 
 
-def committed_traffic(workload: str, digest: str):
-    """HBM bytes per launch from the committed counter summary, if it matches this kernel."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.md")
+def counters_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"attn_fwd_{workload}_counters.md")
+
+
+def committed_counters(workload: str, digest: str):
+    """The machine-readable figures of the committed counter summary of `workload`
+    (written by --summarize-profile), or None if it is missing or was taken on other
+    kernel code (its digest differs)."""
+    path = counters_path(workload)
     if not os.path.exists(path):
         return None
-    text = open(path).read()
-    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    m_t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_d or not m_t or m_d.group(1) != digest:
+    vals = dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", open(path).read(), flags=re.M))
+    if vals.get("kernel_source_digest") != digest:
         return None
-    return float(m_t.group(1))
+    out = {}
+    for key in ("mfma_util", "hbm_bytes_per_launch", "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch",
+                "valu_per_mfma", "lds_per_mfma", "kernel_clock_ghz"):
+        if key in vals:
+            out[key] = float(vals[key])
+    return out
+
+
+def committed_traffic(workload: str, digest: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel."""
+    c = committed_counters(workload, digest)
+    return None if c is None or "hbm_bytes_per_launch" not in c else c["hbm_bytes_per_launch"]
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter passes and their summaries
+# ---------------------------------------------------------------------------
+
+# one pass each (rocprofv3 does not split counters over passes): matrix-core and instruction counters, then
+# the two HBM byte counters on their own
+PMC_MFMA = ["SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+            "SQ_INSTS_SALU", "SQ_WAVES", "SQ_LDS_BANK_CONFLICT"]
+PROFILE_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-mfma-probe", "--no-backward",
+                "--no-decode", "--no-weights", "--no-mha", "--no-workloads"]
+CALIBRATION_BYTES = 256 << 20   # --copy-calibration: a device copy reading and writing this many bytes
+
+
+def profile_commands(workload: str, out_dir: str):
+    """(name, argv) of the rocprofv3 runs behind one counter summary: the program itself after `--`."""
+    bench = [sys.executable, os.path.abspath(__file__), "--workload", workload]
+    runs = [("mfma", ["--pmc", *PMC_MFMA]), ("fetch", ["--pmc", "FETCH_SIZE"]), ("write", ["--pmc", "WRITE_SIZE"])]
+    cmds = []
+    for name, pmc in runs:
+        cmds.append((name, ["rocprofv3", *pmc, "--output-format", "csv", "-d", os.path.join(out_dir, name), "-o", "run",
+                            "--", *bench, *PROFILE_ARGS, "--copy-calibration"]))
+    # kernel time: the default warm-up and timed launches, nothing else
+    cmds.append(("trace", ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                           os.path.join(out_dir, "trace"), "-o", "run", "--", *bench, *PROFILE_ARGS[4:]]))
+    return cmds
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find_csv(d, name):
+    for root, _dirs, files in os.walk(d):
+        if name in files:
+            return os.path.join(root, name)
+    raise FileNotFoundError(f"{name} under {d}")
+
+
+def forward_kernel_name(w) -> str:
+    kind = "attn_fwd_bf16_kernel" if w.dtype == "bf16" else "attn_fwd_f32_kernel"
+    return f"attn::{kind}<{w.d}, {str(w.causal).lower()}, {str(w.keypad).lower()}>"
+
+
+def _per_dispatch(rows, kernel_substr):
+    """{dispatch id: {counter: value}} for the dispatches of one kernel (values summed over dimensions)."""
+    out = {}
+    for r in rows:
+        if kernel_substr in r["Kernel_Name"]:
+            d = out.setdefault(int(r["Dispatch_Id"]), {"_grid": int(r["Grid_Size"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _mean(xs):
+    xs = list(xs)
+    return sum(xs) / len(xs)
+
+
+def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, commands=None) -> str:
+    """Markdown summary of the counter passes under prof_dir (mfma/, fetch/, write/) for the forward
+    kernel of `workload`, ending in machine-readable `key: value` lines that bench.py reads back
+    (committed_counters).  HBM bytes: FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by the
+    factor that makes the same counter read the known bytes of the calibration copy in the same run."""
+    from transformer_scaled_dot_03_amd.workloads import WORKLOADS
+    w = WORKLOADS[workload]
+    kname = forward_kernel_name(w)
+    agent = next(a for a in _read_csv(_find_csv(os.path.join(prof_dir, "mfma"), "run_agent_info.csv"))
+                 if a["Agent_Type"] == "GPU")
+    simds, xcds = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    rows = _read_csv(_find_csv(os.path.join(prof_dir, "mfma"), "run_counter_collection.csv"))
+    disp = _per_dispatch(rows, kname)
+    if not disp:
+        raise ValueError(f"no dispatch of {kname} in {prof_dir}/mfma")
+    missing = [k for k in PMC_MFMA if any(k not in d for d in disp.values())]
+    if missing:
+        raise ValueError(f"counters {missing} missing from {prof_dir}/mfma")
+    c = {k: _mean(d[k] for d in disp.values()) for k in PMC_MFMA}
+    dur_ns = _mean(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]) for r in rows
+                   if kname in r["Kernel_Name"] and r["Counter_Name"] == "GRBM_GUI_ACTIVE")
+    long_dispatch = dur_ns > 100e3
+    busy_per_simd = c["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    cycles_per_xcd = c["GRBM_GUI_ACTIVE"] / xcds
+    util = busy_per_simd / cycles_per_xcd
+    valu_other = c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]   # SQ_INSTS_VALU counts the MFMAs too
+
+    def scaled(sub, counter):
+        rs = _read_csv(_find_csv(os.path.join(prof_dir, sub), "run_counter_collection.csv"))
+        kern = [v[counter] for v in _per_dispatch(rs, kname).values()]
+        copies = _per_dispatch(rs, "copyBuffer")
+        big = max(v["_grid"] for v in copies.values())
+        cal = [v[counter] for v in copies.values() if v["_grid"] == big]
+        factor = (CALIBRATION_BYTES / 1024.0) / _mean(cal)
+        return _mean(kern), factor, _mean(cal)
+
+    # kernel time from the trace pass (when present): every dispatch of the kernel, and the timed ones
+    trace_rows = []
+    tdir = os.path.join(prof_dir, "trace")
+    if os.path.isdir(tdir):
+        trace_rows = [float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+                      for r in _read_csv(_find_csv(tdir, "run_kernel_trace.csv")) if kname in r["Kernel_Name"]]
+    fetch_kib, f_fac, f_cal = scaled("fetch", "FETCH_SIZE")
+    write_kib, w_fac, w_cal = scaled("write", "WRITE_SIZE")
+    rd = fetch_kib * f_fac * 1024.0
+    wr = write_kib * w_fac * 1024.0
+    comp = compulsory_bytes(w)
+    lines = [
+        f"# Counters: {kname} on {workload}",
+        "",
+        f"{w.desc}: B{w.B} h{w.h} Tq={w.Tq} Tk={w.Tk} d={w.d} {w.dtype}, causal={w.causal}, "
+        f"key padding={w.keypad}.  {len(disp)} dispatches of the kernel per pass; means per dispatch.",
+        "",
+        "Commands (repository root on an MI355X host, `TMPDIR=/tmp`); the summary is "
+        f"`python3 bench.py --summarize-profile <out> --workload {workload}`:",
+        "",
+    ]
+    for name, argv in (commands or profile_commands(workload, "<out>")):
+        shown = ["python3" if a == sys.executable else ("bench.py" if a == os.path.abspath(__file__) else a)
+                 for a in argv]
+        lines.append("    " + " ".join(shown))
+    lines += [
+        "",
+        "| Quantity | Value | Reading |",
+        "|---|---|---|",
+        f"| SQ_INSTS_MFMA | {c['SQ_INSTS_MFMA']:.0f} | {c['SQ_INSTS_MFMA'] / c['SQ_WAVES']:.1f} per wave |",
+        f"| SQ_VALU_MFMA_BUSY_CYCLES | {c['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | "
+        f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / c['SQ_INSTS_MFMA']:.1f} busy cycles per MFMA; {busy_per_simd:.0f} per SIMD "
+        f"({simds} SIMDs) |",
+        f"| GRBM_GUI_ACTIVE | {c['GRBM_GUI_ACTIVE']:.0f} | {cycles_per_xcd:.0f} GPU cycles per XCD ({xcds} XCDs)"
+        + (f"; {cycles_per_xcd / dur_ns:.3f} GHz over the {dur_ns / 1e3:.1f} us dispatch |" if long_dispatch else
+           f" over a {dur_ns / 1e3:.1f} us dispatch (too short for a clock figure: the counter also runs "
+           "around the dispatch) |"),
+        f"| MFMA utilisation | {util:.4f} | busy cycles per SIMD / GPU cycles per XCD |",
+        f"| SQ_INSTS_VALU (less MFMA) | {valu_other:.0f} | {valu_other / c['SQ_INSTS_MFMA']:.2f} per MFMA |",
+        f"| SQ_INSTS_LDS | {c['SQ_INSTS_LDS']:.0f} | {c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f} per MFMA |",
+        f"| SQ_INSTS_SALU | {c['SQ_INSTS_SALU']:.0f} | |",
+        f"| SQ_LDS_BANK_CONFLICT | {c['SQ_LDS_BANK_CONFLICT']:.0f} | cycles |",
+        f"| SQ_WAVES | {c['SQ_WAVES']:.0f} | |",
+        f"| FETCH_SIZE | {fetch_kib:.1f} KiB | x {f_fac:.5f} (the calibration copy reads {CALIBRATION_BYTES} bytes, "
+        f"FETCH_SIZE {f_cal:.1f} KiB) = {rd:.0f} bytes read |",
+        f"| WRITE_SIZE | {write_kib:.1f} KiB | x {w_fac:.5f} (calibration WRITE_SIZE {w_cal:.1f} KiB) = {wr:.0f} "
+        f"bytes written |",
+        f"| HBM traffic | {rd + wr:.0f} bytes | {(rd + wr) / comp:.3f} x the compulsory {comp:.0f} (read Q, K, V, "
+        f"write O once) |",
+    ]
+    timed = trace_rows[30:] if len(trace_rows) > 30 else trace_rows
+    if trace_rows:
+        lines += [
+            f"| kernel time (trace pass) | {_mean(timed) / 1e3:.2f} us | mean of the {len(timed)} timed launches "
+            f"(after the 30 warm-up ones); all {len(trace_rows)}: min {min(trace_rows) / 1e3:.2f}, "
+            f"max {max(trace_rows) / 1e3:.2f} us |",
+            f"| metric throughput at that time | {flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12:.1f} TFLOP/s | "
+            f"{flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} of the {PEAK_BF16_TFLOPS:.0f} "
+            f"TFLOP/s dense-bf16 peak ({flops_per_step(w):.4g} metric flops per launch) |",
+        ]
+    lines += [
+        "",
+        f"kernel_source_digest: {digest or kernel_source_digest()}",
+        f"workload: {workload}",
+        f"mfma_util: {util:.4f}",
+        f"valu_per_mfma: {valu_other / c['SQ_INSTS_MFMA']:.3f}",
+        f"lds_per_mfma: {c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.3f}",
+        f"hbm_read_bytes_per_launch: {rd:.0f}",
+        f"hbm_write_bytes_per_launch: {wr:.0f}",
+        f"hbm_bytes_per_launch: {rd + wr:.0f}",
+    ]
+    if long_dispatch:
+        lines.append(f"kernel_clock_ghz: {cycles_per_xcd / dur_ns:.3f}")
+    if trace_rows:
+        lines.append(f"kernel_us: {_mean(timed) / 1e3:.3f}")
+    lines.append("")
+    return "\n".join(lines)
+
+
+def collect_profile(workload: str, out_dir: str) -> str:
+    """Run the counter passes (each rocprofv3 with this program after `--`, under a time limit) and
+    return the summary.  This process itself never touches the GPU."""
+    import subprocess
+    env = dict(os.environ, TMPDIR="/tmp")
+    cmds = profile_commands(workload, out_dir)
+    for name, argv in cmds:
+        print(f"bench.py: counter pass {name} for {workload}", file=sys.stderr, flush=True)
+        r = subprocess.run(["timeout", "-s", "KILL", "180", *argv], cwd="/tmp", env=env,
+                           stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"counter pass {name} failed ({r.returncode}): {r.stderr[-2000:]}")
+    return summarize_profile(workload, out_dir, commands=cmds)
 
 
 def flops_per_step(w) -> float:
@@ -446,8 +651,16 @@ def time_workloads(torch, tsd, names, min_calls=100, min_seconds=1.0, max_calls=
         cb = compulsory_bytes(w)
         r = {"calls": n, "median_ms": round(med, 5), "min_ms": round(mn, 5),
              "tflops": round(fl / (med * 1e-3) / 1e12, 2),
+             "frac": round(fl / (med * 1e-3) / 1e12 / (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS), 4),
              "algorithmic_tflops": round(alg / (med * 1e-3) / 1e12, 2),
              "hbm_GBs": round(cb / (med * 1e-3) / 1e9, 1)}
+        cnt = committed_counters(name, kernel_source_digest())
+        if cnt:
+            # counter figures of this kernel code on this workload (profiles/), rocprofv3 passes
+            r["mfma_util"] = cnt.get("mfma_util")
+            r["hbm_traffic_bytes"] = cnt.get("hbm_bytes_per_launch")
+            if cnt.get("hbm_bytes_per_launch"):
+                r["measured_hbm_GBs"] = round(cnt["hbm_bytes_per_launch"] / (med * 1e-3) / 1e9, 1)
         if cb <= (256 << 20):
             if flush is None:
                 flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device=dev)
@@ -542,7 +755,24 @@ def main():
     ap.add_argument("--decode-workload", default=None)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--collect-profile", metavar="DIR", default=None,
+                    help="run the rocprofv3 counter passes of --workload into DIR and write the summary to "
+                         "profiles/ (this process starts rocprofv3 runs and touches no GPU itself)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="print the summary of counter passes already in DIR (mfma/, fetch/, write/)")
     args = ap.parse_args()
+
+    if args.summarize_profile or args.collect_profile:
+        from transformer_scaled_dot_03_amd.workloads import HEADLINE
+        name = args.workload or HEADLINE
+        if args.collect_profile:
+            text = collect_profile(name, os.path.abspath(args.collect_profile))
+            with open(counters_path(name), "w") as f:
+                f.write(text)
+        else:
+            text = summarize_profile(name, args.summarize_profile)
+        print(text)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU (--gpus 1); multi-GPU runs are not "
@@ -610,7 +840,8 @@ def main():
     achieved = fl / (ev_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     digest = kernel_source_digest()
-    traffic = committed_traffic(name, digest)
+    counters = committed_counters(name, digest) or {}
+    traffic = counters.get("hbm_bytes_per_launch")
     cb = compulsory_bytes(w)
     rec = {
         "metric": METRIC,
@@ -629,8 +860,11 @@ def main():
                    "causal": w.causal, "key_padding": w.keypad, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel_ms": round(ev_ms, 4), "kernel_source_digest": digest},
+                     "kernel_ms": round(ev_ms, 4), "kernel_source_digest": digest,
+                     "mfma_util": counters.get("mfma_util"),
+                     "counters": ("profiles/" + os.path.basename(counters_path(name))) if counters else None},
         "hbm": {"compulsory_bytes": cb, "achieved_GBs": round(cb / (ev_ms * 1e-3) / 1e9, 1),
+                "measured_GBs": round(traffic / (ev_ms * 1e-3) / 1e9, 1) if traffic else None,
                 "peak_GBs": PEAK_HBM_GBS},
     }
     if not args.no_backward and w.dtype == "bf16":

@@ -64,3 +64,99 @@ def test_digest_ignores_comments_but_not_code():
     c = b"int f(int x) { return 3 * x; }\n"
     assert bench.code_only(a) == bench.code_only(b)
     assert bench.code_only(a) != bench.code_only(c)
+
+
+FIXTURE = os.path.join(ROOT, "tests", "golden", "rocprof_enc_self_b32h8t256d64")
+FIX_WORKLOAD = "enc_self_bf16_b32h8t256d64_keypad"
+
+
+def _fixture_rows(sub):
+    import csv
+    with open(os.path.join(FIXTURE, sub, "run_counter_collection.csv"), newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _machine_lines(text):
+    import re
+    return dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", text, flags=re.M))
+
+
+def test_profile_summary_of_a_recorded_rocprofv3_run():
+    """tests/golden/rocprof_enc_self_b32h8t256d64: rocprofv3 CSVs of the encoder key-padding forward
+    (two kernel dispatches per counter pass, the calibration copies, a kernel trace), trimmed from a
+    run of `bench.py --collect-profile` on an MI355X.  The summary must reproduce the figures computed
+    here directly from the rows."""
+    sys.path.insert(0, ROOT)
+    import bench
+    text = bench.summarize_profile(FIX_WORKLOAD, FIXTURE, digest="f" * 16)
+    vals = _machine_lines(text)
+    assert vals["kernel_source_digest"] == "f" * 16 and vals["workload"] == FIX_WORKLOAD
+
+    kern = "attn_fwd_bf16_kernel<64, false, true>"
+    rows = _fixture_rows("mfma")
+
+    def per_dispatch(rs, counter, name):
+        vals_ = {}
+        for r in rs:
+            if name in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                vals_[r["Dispatch_Id"]] = vals_.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return list(vals_.values())
+
+    busy = per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", kern)
+    grbm = per_dispatch(rows, "GRBM_GUI_ACTIVE", kern)
+    assert len(busy) == 2 and len(grbm) == 2
+    # 1024 SIMDs and 8 XCDs, as the agent table of the run says
+    util = (sum(busy) / 2 / 1024) / (sum(grbm) / 2 / 8)
+    assert abs(float(vals["mfma_util"]) - util) < 1e-4
+
+    def scaled(sub, counter):
+        rs = _fixture_rows(sub)
+        k = per_dispatch(rs, counter, kern)
+        grids = {}
+        for r in rs:
+            if "copyBuffer" in r["Kernel_Name"]:
+                grids.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        cal = grids[max(grids)]        # the 256 MiB calibration copies, not the small input copy
+        return (sum(k) / len(k)) * (256 * 1024 / (sum(cal) / len(cal))) * 1024
+
+    rd, wr = scaled("fetch", "FETCH_SIZE"), scaled("write", "WRITE_SIZE")
+    assert abs(float(vals["hbm_read_bytes_per_launch"]) - rd) <= 1.0
+    assert abs(float(vals["hbm_write_bytes_per_launch"]) - wr) <= 1.0
+    assert abs(float(vals["hbm_bytes_per_launch"]) - (rd + wr)) <= 2.0
+    # the output is written once: 2 bytes per element of [32, 8, 256, 64]
+    assert abs(wr - 32 * 8 * 256 * 64 * 2) / wr < 0.01
+    # kernel time from the trace pass: the dispatches after the 30 warm-up launches
+    import csv
+    with open(os.path.join(FIXTURE, "trace", "run_kernel_trace.csv"), newline="") as f:
+        durs = [float(r["End_Timestamp"]) - float(r["Start_Timestamp"]) for r in csv.DictReader(f)]
+    assert abs(float(vals["kernel_us"]) - sum(durs[30:]) / len(durs[30:]) / 1e3) < 1e-3
+
+
+def test_counter_summary_round_trip_is_keyed_to_the_kernel_source(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    digest = bench.kernel_source_digest()
+    with open(bench.counters_path(FIX_WORKLOAD), "w") as f:
+        f.write(bench.summarize_profile(FIX_WORKLOAD, FIXTURE, digest=digest))
+    got = bench.committed_counters(FIX_WORKLOAD, digest)
+    vals = _machine_lines(open(bench.counters_path(FIX_WORKLOAD)).read())
+    assert got["mfma_util"] == float(vals["mfma_util"])
+    assert bench.committed_traffic(FIX_WORKLOAD, digest) == float(vals["hbm_bytes_per_launch"])
+    # figures taken on other kernel code are not reported
+    assert bench.committed_counters(FIX_WORKLOAD, "0" * 16) is None
+
+
+def test_profile_commands_put_the_program_right_after_the_double_dash():
+    sys.path.insert(0, ROOT)
+    import bench
+    cmds = bench.profile_commands(FIX_WORKLOAD, "/tmp/x")
+    assert [n for n, _ in cmds] == ["mfma", "fetch", "write", "trace"]
+    for name, argv in cmds:
+        assert argv[0] == "rocprofv3"
+        i = argv.index("--")
+        assert argv[i + 1] == sys.executable and argv[i + 2].endswith("bench.py")
+        if name == "trace":
+            assert "--kernel-trace" in argv and "--pmc" not in argv
+        else:
+            assert "--pmc" in argv and not any(a in argv for a in ("-s", "--sys-trace", "-r", "--runtime-trace"))
