@@ -297,10 +297,11 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
     ]
     timed = trace_rows[30:] if len(trace_rows) > 30 else trace_rows
     if trace_rows:
+        first = trace_rows[:20]
         lines += [
             f"| kernel time (trace pass) | {_mean(timed) / 1e3:.2f} us | mean of the {len(timed)} timed launches "
-            f"(after the 30 warm-up ones); all {len(trace_rows)}: min {min(trace_rows) / 1e3:.2f}, "
-            f"max {max(trace_rows) / 1e3:.2f} us |",
+            f"(after the 30 warm-up ones, back to back); all {len(trace_rows)}: min {min(trace_rows) / 1e3:.2f}, "
+            f"max {max(trace_rows) / 1e3:.2f} us; launches 1-{len(first)}: mean {_mean(first) / 1e3:.2f} us |",
             f"| metric throughput at that time | {flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12:.1f} TFLOP/s | "
             f"{flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} of the {PEAK_BF16_TFLOPS:.0f} "
             f"TFLOP/s dense-bf16 peak ({flops_per_step(w):.4g} metric flops per launch) |",
