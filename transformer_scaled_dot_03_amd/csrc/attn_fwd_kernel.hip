@@ -325,17 +325,19 @@ __global__ __launch_bounds__(64 * Bf16Shape<D>::kWaves, Bf16Shape<D>::kMinWaves)
     float m_tile[RG];
     auto row_max = [&](int j0, f32x16 (&sc)[RG][NH], auto MASKED) -> bool {
       if (decltype(MASKED)::value && ((j0 + BN > kend) || (CAUSAL && j0 + BN - 1 > qw))) {
+        // key j0 + 8g + off(e) is allowed iff off(e) < lim - j0 - 8g, lim =
+        // min(kend, row + 1): one compare against a constant per score
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
+        for (int r = 0; r < RG; ++r) {
+          int lim = kend;
+          if (CAUSAL) lim = min(lim, qw + 32 * r + c + 1);
+          const int rel = lim - j0 - 8 * g;
 #pragma unroll
           for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = j0 + 32 * hh + 16 * (e >> 3) + 8 * g + (e & 7);
-              bool ok = key < kend;
-              if (CAUSAL) ok = ok && key <= qw + 32 * r + c;
-              sc[r][hh][e] = ok ? sc[r][hh][e] : kNegInf;
-            }
+            for (int e = 0; e < 16; ++e)
+              sc[r][hh][e] = (32 * hh + 16 * (e >> 3) + (e & 7)) < rel ? sc[r][hh][e] : kNegInf;
+        }
       }
       // IEEE maximum (NaN-propagating): gfx950's v_maximum3_f32, with no
       // canonicalising moves in front of it (a NaN score makes the row NaN
