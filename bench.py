@@ -262,13 +262,25 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
         f"{w.desc}: B{w.B} h{w.h} Tq={w.Tq} Tk={w.Tk} d={w.d} {w.dtype}, causal={w.causal}, "
         f"key padding={w.keypad}.  {len(disp)} dispatches of the kernel per pass; means per dispatch.",
         "",
-        "Commands (repository root on an MI355X host, `TMPDIR=/tmp`); the summary is "
+        f"Commands: `python3 bench.py --workload {workload} --collect-profile <out>` on an MI355X host "
+        "runs these passes, each from /tmp with `TMPDIR=/tmp` (bench.py is the repository's, by its "
+        "absolute path); the summary is "
         f"`python3 bench.py --summarize-profile <out> --workload {workload}`:",
         "",
     ]
+    out_prefix = os.path.abspath(prof_dir)
+
+    def show(a):
+        if a == sys.executable:
+            return "python3"
+        if a == os.path.abspath(__file__):
+            return "bench.py"
+        if os.path.isabs(a) and (a == out_prefix or a.startswith(out_prefix + os.sep)):
+            return "<out>" + a[len(out_prefix):]
+        return a
+
     for name, argv in (commands or profile_commands(workload, "<out>")):
-        shown = ["python3" if a == sys.executable else ("bench.py" if a == os.path.abspath(__file__) else a)
-                 for a in argv]
+        shown = [show(a) for a in argv]
         lines.append("    " + " ".join(shown))
     lines += [
         "",

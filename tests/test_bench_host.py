@@ -160,3 +160,16 @@ def test_profile_commands_put_the_program_right_after_the_double_dash():
             assert "--kernel-trace" in argv and "--pmc" not in argv
         else:
             assert "--pmc" in argv and not any(a in argv for a in ("-s", "--sys-trace", "-r", "--runtime-trace"))
+
+
+def test_summary_shows_the_output_directory_as_a_placeholder():
+    """The passes write under an absolute directory of the host that ran them; the committed summary
+    names it `<out>`, the argument given to --collect-profile."""
+    sys.path.insert(0, ROOT)
+    import bench
+    text = bench.summarize_profile(FIX_WORKLOAD, FIXTURE, digest="f" * 16,
+                                   commands=bench.profile_commands(FIX_WORKLOAD, FIXTURE))
+    assert FIXTURE not in text and os.path.abspath(FIXTURE) not in text
+    for sub in ("mfma", "fetch", "write", "trace"):
+        assert f"-d <out>/{sub} " in text
+    assert "-- python3 bench.py --workload " + FIX_WORKLOAD in text
