@@ -90,14 +90,6 @@ __device__ __forceinline__ void tr_offsets(int lane, int (&rd)[BwdTile<D>::NO][2
   }
 }
 
-// base ^ imm computed where it is used: an asm the compiler cannot hoist, so a
-// set of per-step LDS offsets costs one register instead of one each
-__device__ __forceinline__ int xor_at_use(int base, int imm) {
-  int r;
-  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(imm), "v"(base));
-  return r;
-}
-
 // A operand (8 consecutive rows of the transposed tile) from two transposed reads
 __device__ __forceinline__ bf16x8 tr_fragment(const char* lo_addr, const char* hi_addr) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lo_addr));
@@ -297,25 +289,55 @@ struct DkdvShape {
   static constexpr bool kVInLds = D == 128;
 };
 
+// Q / dO tiles of the d = 128 dK/dV kernel: 64 rows of 256 bytes, row r at
+// byte 288 r + 16 ((r >> 3) & 1) of the tile (a 288-byte slot per row, the row
+// shifted by 16 bytes when bit 3 of r is set).  Both read patterns are free of
+// bank conflicts -- 16-byte fragments of 16 rows in sigma order (16 distinct
+// 16-byte bank groups) and transposed reads of 4 consecutive rows at two chunk
+// columns 128 bytes apart (32 distinct 8-byte groups) -- and, unlike an XOR
+// swizzle, the offset of every step is a constant added to one per-lane base,
+// so the reads cost no address arithmetic.  The 32 spare bytes per row are
+// filled by loads past the buffer's range (zeros, no memory access).
+struct PadTile128 {
+  static constexpr int SLOT = 288;
+  static constexpr int BYTES = 64 * SLOT;        // 18 KB
+  static constexpr int UNITS = BYTES / 1024;     // 1 KB direct-to-LDS loads per tile
+  __device__ static constexpr int row(int r) { return SLOT * r + 16 * ((r >> 3) & 1); }
+  // source offset (row-major 256-byte rows) of the 16 bytes at tile byte pos, or pad for a gap
+  __device__ static uint32_t src(int pos, uint32_t pad) {
+    const int r = pos / SLOT, k = pos - row(r);
+    return (k >= 0 && k < 256) ? (uint32_t)(r * 256 + k) : pad;
+  }
+};
+// V rows of the d = 128 dK/dV work-group (256 keys): row r at byte 272 r; each
+// lane reads only its own key's row, 16 consecutive rows per 16 lanes, which
+// the 272-byte stride spreads over all 64 banks
+constexpr int kVRowSlot = 272;
+
+// launder a value through an empty asm: the compiler can no longer split a
+// constant out of it, so base + small constant stays one LDS offset field
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int D, bool CAUSAL, bool KEYPAD>
 __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   using TG = BwdTile<D>;
   constexpr int W = DkdvShape<D>::kWaves;
   constexpr bool VLDS = DkdvShape<D>::kVInLds;
-  constexpr int ROWB = TG::ROWB, TILEB = TG::TILEB, DT = TG::DT, NO = TG::NO;
-  constexpr int NLD = TILEB / 1024 / W;
+  static_assert(!VLDS || D == 128, "the padded layout is laid out for d = 128");
+  constexpr int ROWB = TG::ROWB, DT = TG::DT, NO = TG::NO;
   constexpr int BK = 32 * W;
-  static_assert(NLD >= 1, "tile shape");
-
-  __shared__ __attribute__((aligned(1024))) char qb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char qb1[TILEB];
-  __shared__ __attribute__((aligned(1024))) char gb0[TILEB];
-  __shared__ __attribute__((aligned(1024))) char gb1[TILEB];
-  // per tile: lse * log2(e) of its 64 rows in [0, 64), D in [64, 128)
-  __shared__ __attribute__((aligned(256))) float rb0[128];
-  __shared__ __attribute__((aligned(256))) float rb1[128];
-  // V rows of the work-group's keys: chunk k of row r at k ^ (r % 16)
-  __shared__ __attribute__((aligned(1024))) char vrows[VLDS ? BK * ROWB : 16];
+  // LDS block: Q tile 0, Q tile 1, dO tile 0, dO tile 1, (d = 128) the V rows,
+  // then per tile the lse * log2(e) of its 64 rows in [0, 64) and D in [64, 128)
+  constexpr int TB = VLDS ? PadTile128::BYTES : TG::TILEB;
+  constexpr int NLD = VLDS ? (PadTile128::UNITS + W - 1) / W : TG::TILEB / 1024 / W;
+  constexpr int VROWSB = VLDS ? BK * kVRowSlot : 0;
+  constexpr int VUNITS = VROWSB / 1024;
+  static_assert(VROWSB % 1024 == 0 && NLD >= 1, "tile shape");
+  constexpr int RB = 4 * TB + VROWSB;   // lse / D of tile u at RB + 512 u
+  __shared__ __attribute__((aligned(1024))) char lds[RB + 1024];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -340,50 +362,100 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
   // this lane's key row: K negated for a negative scale (S = scale Q K^T), and V
   bf16x8 kf[DT], vf[VLDS ? 1 : DT];
   load_row<D>(static_cast<const __bf16*>(p.k) + koff, key, kend, g, p.neg != 0, kf);
-  int vbase = 0;
+  int vb = 0;
   if constexpr (VLDS) {
-    // the work-group's V rows into LDS once (rows at or past kend read as zero)
+    // the work-group's V rows into LDS once (rows at or past kend, and the
+    // spare bytes of each slot, read as zero)
     const __bf16* Vb = static_cast<const __bf16*>(p.v) + koff + (int64_t)k0 * D;
     const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(Vb, (uint32_t)max(min(kend - k0, BK), 0) * ROWB);
 #pragma unroll
-    for (int u = 0; u < BK * ROWB / 1024 / W; ++u) {
-      const int pos = (W * u + w) * 1024 + 16 * lane;
-      const int r = pos / ROWB, sc = (pos % ROWB) / 16;
-      lds_dma16(vr, vrows + (W * u + w) * 1024, r * ROWB + 16 * (sc ^ (r & 15)));
+    for (int u = 0; u < (VUNITS + W - 1) / W; ++u) {
+      const int unit = W * u + w;
+      if (unit < VUNITS) {
+        const int pos = unit * 1024 + 16 * lane;
+        const int r = pos / kVRowSlot, k = pos - r * kVRowSlot;
+        lds_dma16(vr, lds + 4 * TB + unit * 1024, k < ROWB ? (uint32_t)(r * ROWB + k) : (uint32_t)(BK * ROWB));
+      }
     }
-    // chunk 2t + g of row 32w + c sits at (2t + g) ^ (c % 16): one base XOR 32 t
-    vbase = (32 * w + c) * ROWB + 16 * (g ^ (c & 1)) + 32 * ((c & 15) >> 1);
+    // chunk 2t + g of row 32w + c: base + 32 t
+    vb = opaque(4 * TB + (32 * w + c) * kVRowSlot + 16 * g);
   } else {
     load_row<D>(static_cast<const __bf16*>(p.v) + koff, key, kend, g, false, vf);
   }
 
   uint32_t src[NLD];
-  tile_src_offsets<D, W>(w, lane, src);
-  auto load_tile = [&](int r0, char* qt, char* gt, float* rt) __attribute__((always_inline)) {
-    const uint32_t bytes = (uint32_t)(Tq - r0) * ROWB;
+  if constexpr (VLDS) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) src[u] = PadTile128::src((W * u + w) * 1024 + 16 * lane, 64 * ROWB);
+  } else {
+    tile_src_offsets<D, W>(w, lane, src);
+  }
+  // tile buffers by index: Q tile u at u * TB, dO tile u at (2 + u) * TB
+  auto load_tile = [&](int r0, int u) __attribute__((always_inline)) {
+    // the buffer range covers this tile's rows only, so a pad offset of 64 rows is always past it
+    const uint32_t bytes = (uint32_t)min(Tq - r0, kBT) * ROWB;
     const __amdgpu_buffer_rsrc_t qr = buffer_rsrc(Qg + (int64_t)r0 * D, bytes);
     const __amdgpu_buffer_rsrc_t gr = buffer_rsrc(Gg + (int64_t)r0 * D, bytes);
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      lds_dma16(qr, qt + (W * u + w) * 1024, src[u]);
-      lds_dma16(gr, gt + (W * u + w) * 1024, src[u]);
+    for (int v = 0; v < NLD; ++v) {
+      const int unit = W * v + w;
+      if (!VLDS || unit < PadTile128::UNITS) {
+        lds_dma16(qr, lds + u * TB + unit * 1024, src[v]);
+        lds_dma16(gr, lds + (2 + u) * TB + unit * 1024, src[v]);
+      }
     }
     // lse * log2(e) (wave 0) and D (wave 1) of rows r0 .. r0 + 63; rows at or past Tq read as 0
     if (w < 2) {
       const __amdgpu_buffer_rsrc_t rr = buffer_rsrc(w == 0 ? Lg + r0 : Dg + r0, (uint32_t)(Tq - r0) * 4);
-      lds_dma4(rr, reinterpret_cast<char*>(rt) + 256 * w, 4 * lane);
+      lds_dma4(rr, lds + RB + 512 * u + 256 * w, 4 * lane);
     }
   };
-  int fr[DT];
-  frag_offsets<D>(c, g, fr);
-  int trd[NO][2];
-  tr_offsets<D>(lane, trd);
-  // with d = 128 the step offsets are base ^ 32 t (fragment reads, V rows) and
-  // base ^ 32 i (transposed reads): keep the bases only (two waves share a SIMD)
-  const int fbase = fr[0], tb0 = trd[0][0], tb1 = trd[0][1];
-  auto frag_at = [&](int t) __attribute__((always_inline)) { return VLDS ? xor_at_use(fbase, 32 * t) : fr[t]; };
-  auto tr_at = [&](int i, int e) __attribute__((always_inline)) {
-    return VLDS ? xor_at_use(e ? tb1 : tb0, 32 * i) : trd[i][e];
+  // per-lane read offsets.  d = 128: one base per pattern and tensor, every
+  // step a constant on top (fragment: row 32 hh + sigma(c), chunk 2t + g;
+  // transposed: row 32 hh + 16 m + 8 gg + 4 e + s / 4, chunk 8 (s & 1) + 2 i + h,
+  // half (s >> 1) & 1, for 16-lane group G = 2 gg + h and source lane s); the
+  // dO bases carry the dO buffers' offset so their constants stay small.
+  // d = 64: the XOR-swizzled offsets of every step held in registers.
+  int fr[VLDS ? 1 : DT];
+  int trd[VLDS ? 1 : NO][2];
+  int fbq = 0, fbg = 0, tbq = 0, tbg = 0;
+  if constexpr (VLDS) {
+    const int sl = lane & 15, G = lane >> 4, h = G & 1, gg = G >> 1;
+    fbq = PadTile128::row(sigma32(c)) + 16 * g;
+    tbq = PadTile128::row(8 * gg + (sl >> 2)) + 128 * (sl & 1) + 16 * h + 8 * ((sl >> 1) & 1);
+    fbg = opaque(fbq + 2 * TB);
+    tbg = opaque(tbq + 2 * TB);
+  } else {
+    frag_offsets<D>(c, g, fr);
+    tr_offsets<D>(lane, trd);
+  }
+  // Q / dO fragment of row 32 hh + sigma(c), step t, from buffer u
+  auto q_frag = [&](int u, int hh, int t) __attribute__((always_inline)) {
+    if constexpr (VLDS) return *reinterpret_cast<const bf16x8*>(lds + fbq + u * TB + 32 * PadTile128::SLOT * hh + 32 * t);
+    else return *reinterpret_cast<const bf16x8*>(lds + u * TB + 32 * hh * ROWB + fr[t]);
+  };
+  auto g_frag = [&](int u, int hh, int t) __attribute__((always_inline)) {
+    if constexpr (VLDS) return *reinterpret_cast<const bf16x8*>(lds + fbg + u * TB + 32 * PadTile128::SLOT * hh + 32 * t);
+    else return *reinterpret_cast<const bf16x8*>(lds + (2 + u) * TB + 32 * hh * ROWB + fr[t]);
+  };
+  // transposed A operand (8 rows 16 m' .. of the tile at row block rb = 32 hh + 16 m) for output tile i
+  auto q_tr = [&](int u, int rb, int i) __attribute__((always_inline)) {
+    if constexpr (VLDS) {
+      const char* a = lds + tbq + u * TB + PadTile128::SLOT * rb + 32 * i;
+      return tr_fragment(a, a + 4 * PadTile128::SLOT);
+    } else {
+      const char* a = lds + u * TB + rb * ROWB;
+      return tr_fragment(a + trd[i][0], a + trd[i][1]);
+    }
+  };
+  auto g_tr = [&](int u, int rb, int i) __attribute__((always_inline)) {
+    if constexpr (VLDS) {
+      const char* a = lds + tbg + u * TB + PadTile128::SLOT * rb + 32 * i;
+      return tr_fragment(a, a + 4 * PadTile128::SLOT);
+    } else {
+      const char* a = lds + (2 + u) * TB + rb * ROWB;
+      return tr_fragment(a + trd[i][0], a + trd[i][1]);
+    }
   };
 
   f32x16 adk[NO], adv[NO];
@@ -391,7 +463,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
   for (int i = 0; i < NO; ++i) adk[i] = adv[i] = f32x16{};
   const float cs = p.scale_log2;
 
-  auto step = [&](int it, const char* qt, const char* gt, const float* rt) __attribute__((always_inline)) {
+  // lse / D reads: rows 8g .. 8g + 7 of a 16-row group, from one laundered base
+  const int rbl = opaque(RB + 32 * g);
+  auto step = [&](int it, int u) __attribute__((always_inline)) {
+    const char* rt = lds + rbl + 512 * u;
     const int r0 = it * kBT;
     const bool edge = (kw + 32 > kend) || (CAUSAL && r0 < kw + 31) || (r0 + kBT > Tq);
 #pragma unroll
@@ -399,11 +474,10 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + 32 * hh * ROWB + frag_at(t));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[t], s, 0, 0, 0);
-        const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gt + 32 * hh * ROWB + frag_at(t));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_frag(u, hh, t), kf[t], s, 0, 0, 0);
+        const bf16x8 ga = g_frag(u, hh, t);
         bf16x8 vt;
-        if constexpr (VLDS) vt = *reinterpret_cast<const bf16x8*>(vrows + xor_at_use(vbase, 32 * t));
+        if constexpr (VLDS) vt = *reinterpret_cast<const bf16x8*>(lds + vb + 32 * t);
         else vt = vf[t];
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vt, dp, 0, 0, 0);
       }
@@ -411,10 +485,11 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int rl = 32 * hh + 16 * m + 8 * g;   // first of the 8 rows (tile-local)
-        const f32x4 la = *reinterpret_cast<const f32x4*>(rt + rl);
-        const f32x4 lb = *reinterpret_cast<const f32x4*>(rt + rl + 4);
-        const f32x4 da = *reinterpret_cast<const f32x4*>(rt + 64 + rl);
-        const f32x4 db = *reinterpret_cast<const f32x4*>(rt + 64 + rl + 4);
+        const int ro = 4 * (32 * hh + 16 * m);        // byte offset of the 16-row group
+        const f32x4 la = *reinterpret_cast<const f32x4*>(rt + ro);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(rt + ro + 16);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(rt + 256 + ro);
+        const f32x4 db = *reinterpret_cast<const f32x4*>(rt + 256 + ro + 16);
         f32x8 p8, d8;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -439,33 +514,30 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
         }
         const bf16x8 pb = __builtin_convertvector(p8, bf16x8);
         const bf16x8 dsb = __builtin_convertvector(d8, bf16x8);
-        const char* gtm = gt + (32 * hh + 16 * m) * ROWB;
-        const char* qtm = qt + (32 * hh + 16 * m) * ROWB;
 #pragma unroll
         for (int i = 0; i < NO; ++i) {
-          const int o0 = tr_at(i, 0), o1 = tr_at(i, 1);
-          adv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(gtm + o0, gtm + o1), pb, adv[i], 0, 0, 0);
-          adk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qtm + o0, qtm + o1), dsb, adk[i], 0, 0, 0);
+          adv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g_tr(u, 32 * hh + 16 * m, i), pb, adv[i], 0, 0, 0);
+          adk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_tr(u, 32 * hh + 16 * m, i), dsb, adk[i], 0, 0, 0);
         }
       }
     }
   };
 
-  if (ntiles > 0) load_tile(first * kBT, qb0, gb0, rb0);
+  if (ntiles > 0) load_tile(first * kBT, 0);
   pipeline_barrier<0>();
   // pairs of tiles with no condition around the accumulating steps (a
   // conditional step makes the compiler shuttle dK and dV between register
   // files at every trip), then the odd last tile
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    load_tile((first + it + 1) * kBT, qb1, gb1, rb1);
-    step(first + it, qb0, gb0, rb0);
+    load_tile((first + it + 1) * kBT, 1);
+    step(first + it, 0);
     pipeline_barrier<0>();
-    if (it + 2 < ntiles) load_tile((first + it + 2) * kBT, qb0, gb0, rb0);
-    step(first + it + 1, qb1, gb1, rb1);
+    if (it + 2 < ntiles) load_tile((first + it + 2) * kBT, 0);
+    step(first + it + 1, 1);
     pipeline_barrier<0>();
   }
-  if (it < ntiles) step(first + it, qb0, gb0, rb0);
+  if (it < ntiles) step(first + it, 0);
   if (key < Tk) {
     store_row<D>(static_cast<__bf16*>(p.dk) + koff, key, g, p.scale, adk);
     store_row<D>(static_cast<__bf16*>(p.dv) + koff, key, g, 1.0f, adv);
