@@ -56,6 +56,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 # what the forward kernel is compiled from: its source, the device helpers it
 # includes and its argument struct (the rest of attn_launch.h declares other kernels)
 KERNEL_SOURCES = ["attn_fwd_kernel.hip", "attn_device.h"]
+BWD_KERNEL_SOURCES = ["attn_bwd_kernel.hip", "attn_device.h"]
+# kernels with committed counter summaries: the forward, and the two backward kernels
+PROFILE_KERNELS = ("fwd", "bwd_dq", "bwd_dkdv")
 
 # the forward workloads timed one by one in the `workloads` object (decode workloads are
 # measured by their own kernels)
@@ -73,17 +76,23 @@ def code_only(src: bytes) -> bytes:
     return " ".join(text.split()).encode()
 
 
-def kernel_source_digest() -> str:
-    """Short hash of the forward kernel's code (keys the committed counter data)."""
+def kernel_source_digest(kind: str = "fwd") -> str:
+    """Short hash of the code of the forward kernel (kind "fwd") or of the two backward kernels
+    ("bwd"): keys the committed counter data."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transformer_scaled_dot_03_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in (KERNEL_SOURCES if kind == "fwd" else BWD_KERNEL_SOURCES):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + code_only(f.read()))
     launch = open(os.path.join(csrc, "attn_launch.h"), "rb").read()
-    m = re.search(rb"struct Params \{.*?\};", launch, flags=re.S)
-    h.update(b"Params\0" + code_only(m.group(0) if m else launch))
+    struct = b"Params" if kind == "fwd" else b"BwdParams"
+    m = re.search(rb"struct " + struct + rb" \{.*?\};", launch, flags=re.S)
+    h.update(struct + b"\0" + code_only(m.group(0) if m else launch))
     return h.hexdigest()[:16]
+
+
+def digest_kind(kernel: str) -> str:
+    return "fwd" if kernel == "fwd" else "bwd"
 
 
 def mfma_ceiling(torch, dev, blocks=512, iters=5000, reps=3):
@@ -121,15 +130,16 @@ def mfma_ceiling(torch, dev, blocks=512, iters=5000, reps=3):
     return best
 
 
-def counters_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"attn_fwd_{workload}_counters.md")
+def counters_path(workload: str, kernel: str = "fwd") -> str:
+    prefix = {"fwd": "attn_fwd", "bwd_dq": "attn_bwd_dq", "bwd_dkdv": "attn_bwd_dkdv"}[kernel]
+    return os.path.join(PROFILES, f"{prefix}_{workload}_counters.md")
 
 
-def committed_counters(workload: str, digest: str):
-    """The machine-readable figures of the committed counter summary of `workload`
+def committed_counters(workload: str, digest: str, kernel: str = "fwd"):
+    """The machine-readable figures of the committed counter summary of `kernel` on `workload`
     (written by --summarize-profile), or None if it is missing or was taken on other
     kernel code (its digest differs)."""
-    path = counters_path(workload)
+    path = counters_path(workload, kernel)
     if not os.path.exists(path):
         return None
     vals = dict(re.findall(r"^([a-z_]+):\s*(\S+)\s*$", open(path).read(), flags=re.M))
@@ -137,7 +147,7 @@ def committed_counters(workload: str, digest: str):
         return None
     out = {}
     for key in ("mfma_util", "hbm_bytes_per_launch", "hbm_read_bytes_per_launch", "hbm_write_bytes_per_launch",
-                "valu_per_mfma", "lds_per_mfma", "kernel_clock_ghz"):
+                "valu_per_mfma", "lds_per_mfma", "kernel_clock_ghz", "kernel_us"):
         if key in vals:
             out[key] = float(vals[key])
     return out
@@ -162,17 +172,19 @@ PROFILE_ARGS = ["--steps", "3", "--warmup", "1", "--no-cpu-baseline", "--no-mfma
 CALIBRATION_BYTES = 256 << 20   # --copy-calibration: a device copy reading and writing this many bytes
 
 
-def profile_commands(workload: str, out_dir: str):
-    """(name, argv) of the rocprofv3 runs behind one counter summary: the program itself after `--`."""
+def profile_commands(workload: str, out_dir: str, backward: bool = False):
+    """(name, argv) of the rocprofv3 runs behind one counter summary: the program itself after `--`.
+    With backward=True the runs also time attn_bwd (both backward kernels) after the forward."""
     bench = [sys.executable, os.path.abspath(__file__), "--workload", workload]
+    args = [a for a in PROFILE_ARGS if not (backward and a == "--no-backward")]
     runs = [("mfma", ["--pmc", *PMC_MFMA]), ("fetch", ["--pmc", "FETCH_SIZE"]), ("write", ["--pmc", "WRITE_SIZE"])]
     cmds = []
     for name, pmc in runs:
         cmds.append((name, ["rocprofv3", *pmc, "--output-format", "csv", "-d", os.path.join(out_dir, name), "-o", "run",
-                            "--", *bench, *PROFILE_ARGS, "--copy-calibration"]))
+                            "--", *bench, *args, "--copy-calibration"]))
     # kernel time: the default warm-up and timed launches, nothing else
     cmds.append(("trace", ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
-                           os.path.join(out_dir, "trace"), "-o", "run", "--", *bench, *PROFILE_ARGS[4:]]))
+                           os.path.join(out_dir, "trace"), "-o", "run", "--", *bench, *args[4:]]))
     return cmds
 
 
@@ -194,6 +206,29 @@ def forward_kernel_name(w) -> str:
     return f"attn::{kind}<{w.d}, {str(w.causal).lower()}, {str(w.keypad).lower()}>"
 
 
+def profiled_kernel_name(w, kernel: str) -> str:
+    if kernel == "fwd":
+        return forward_kernel_name(w)
+    kind = {"bwd_dq": "attn_bwd_dq_kernel", "bwd_dkdv": "attn_bwd_dkdv_kernel"}[kernel]
+    return f"attn::{kind}<{w.d}, {str(w.causal).lower()}, {str(w.keypad).lower()}>"
+
+
+def kernel_bytes_and_flops(w, kernel: str):
+    """(compulsory HBM bytes, what they are, flops per launch, what they count) of one launch of
+    the profiled kernel on workload w (bf16 tensors, fp32 lse / D)."""
+    rows, keys = w.B * w.h * w.Tq, w.B * w.h * w.Tk
+    if kernel == "fwd":
+        return (compulsory_bytes(w), "read Q, K, V, write O once", flops_per_step(w),
+                "metric flops: 4 d per allowed pair")
+    if kernel == "bwd_dq":
+        return (2 * w.d * (3 * rows + 2 * keys) + 4 * rows + 2 * w.d * rows + 8 * rows,
+                "read Q, dO, O, K, V and lse, write dQ and the per-row D and lse log2(e) once",
+                1.5 * flops_per_step(w), "executed flops: S, dP and dQ, 6 d per allowed pair")
+    return (2 * w.d * (2 * rows + 2 * keys) + 8 * rows + 2 * w.d * 2 * keys,
+            "read Q, dO, K, V and the per-row D and lse log2(e), write dK and dV once",
+            2.0 * flops_per_step(w), "executed flops: S, dP, dV and dK, 8 d per allowed pair")
+
+
 def _per_dispatch(rows, kernel_substr):
     """{dispatch id: {counter: value}} for the dispatches of one kernel (values summed over dimensions)."""
     out = {}
@@ -209,14 +244,15 @@ def _mean(xs):
     return sum(xs) / len(xs)
 
 
-def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, commands=None) -> str:
+def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, commands=None,
+                      kernel: str = "fwd") -> str:
     """Markdown summary of the counter passes under prof_dir (mfma/, fetch/, write/) for the forward
     kernel of `workload`, ending in machine-readable `key: value` lines that bench.py reads back
     (committed_counters).  HBM bytes: FETCH_SIZE and WRITE_SIZE per dispatch (KiB), each scaled by the
     factor that makes the same counter read the known bytes of the calibration copy in the same run."""
     from transformer_scaled_dot_03_amd.workloads import WORKLOADS
     w = WORKLOADS[workload]
-    kname = forward_kernel_name(w)
+    kname = profiled_kernel_name(w, kernel)
     agent = next(a for a in _read_csv(_find_csv(os.path.join(prof_dir, "mfma"), "run_agent_info.csv"))
                  if a["Agent_Type"] == "GPU")
     simds, xcds = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
@@ -255,17 +291,19 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
     write_kib, w_fac, w_cal = scaled("write", "WRITE_SIZE")
     rd = fetch_kib * f_fac * 1024.0
     wr = write_kib * w_fac * 1024.0
-    comp = compulsory_bytes(w)
+    comp, comp_what, kflops, flops_what = kernel_bytes_and_flops(w, kernel)
+    pk = "" if kernel == "fwd" else " --profile-kernel bwd"
     lines = [
         f"# Counters: {kname} on {workload}",
         "",
         f"{w.desc}: B{w.B} h{w.h} Tq={w.Tq} Tk={w.Tk} d={w.d} {w.dtype}, causal={w.causal}, "
         f"key padding={w.keypad}.  {len(disp)} dispatches of the kernel per pass; means per dispatch.",
         "",
-        f"Commands: `python3 bench.py --workload {workload} --collect-profile <out>` on an MI355X host "
+        f"Commands: `python3 bench.py --workload {workload} --collect-profile <out>{pk}` on an MI355X host "
         "runs these passes, each from /tmp with `TMPDIR=/tmp` (bench.py is the repository's, by its "
         "absolute path); the summary is "
-        f"`python3 bench.py --summarize-profile <out> --workload {workload}`:",
+        f"`python3 bench.py --summarize-profile <out> --workload {workload}"
+        + ("" if kernel == "fwd" else f" --profile-kernel {kernel}") + "`:",
         "",
     ]
     out_prefix = os.path.abspath(prof_dir)
@@ -279,7 +317,7 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
             return "<out>" + a[len(out_prefix):]
         return a
 
-    for name, argv in (commands or profile_commands(workload, "<out>")):
+    for name, argv in (commands or profile_commands(workload, "<out>", backward=kernel != "fwd")):
         shown = [show(a) for a in argv]
         lines.append("    " + " ".join(shown))
     lines += [
@@ -304,8 +342,7 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
         f"FETCH_SIZE {f_cal:.1f} KiB) = {rd:.0f} bytes read |",
         f"| WRITE_SIZE | {write_kib:.1f} KiB | x {w_fac:.5f} (calibration WRITE_SIZE {w_cal:.1f} KiB) = {wr:.0f} "
         f"bytes written |",
-        f"| HBM traffic | {rd + wr:.0f} bytes | {(rd + wr) / comp:.3f} x the compulsory {comp:.0f} (read Q, K, V, "
-        f"write O once) |",
+        f"| HBM traffic | {rd + wr:.0f} bytes | {(rd + wr) / comp:.3f} x the compulsory {comp:.0f} ({comp_what}) |",
     ]
     timed = trace_rows[30:] if len(trace_rows) > 30 else trace_rows
     if trace_rows:
@@ -314,14 +351,16 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
             f"| kernel time (trace pass) | {_mean(timed) / 1e3:.2f} us | mean of the {len(timed)} timed launches "
             f"(after the 30 warm-up ones, back to back); all {len(trace_rows)}: min {min(trace_rows) / 1e3:.2f}, "
             f"max {max(trace_rows) / 1e3:.2f} us; launches 1-{len(first)}: mean {_mean(first) / 1e3:.2f} us |",
-            f"| metric throughput at that time | {flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12:.1f} TFLOP/s | "
-            f"{flops_per_step(w) / (_mean(timed) * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} of the {PEAK_BF16_TFLOPS:.0f} "
-            f"TFLOP/s dense-bf16 peak ({flops_per_step(w):.4g} metric flops per launch) |",
+            f"| {'metric' if kernel == 'fwd' else 'executed'} throughput at that time | "
+            f"{kflops / (_mean(timed) * 1e-9) / 1e12:.1f} TFLOP/s | "
+            f"{kflops / (_mean(timed) * 1e-9) / 1e12 / PEAK_BF16_TFLOPS:.4f} of the {PEAK_BF16_TFLOPS:.0f} "
+            f"TFLOP/s dense-bf16 peak ({kflops:.4g} {flops_what}) |",
         ]
     lines += [
         "",
-        f"kernel_source_digest: {digest or kernel_source_digest()}",
+        f"kernel_source_digest: {digest or kernel_source_digest(digest_kind(kernel))}",
         f"workload: {workload}",
+        f"kernel: {kernel}",
         f"mfma_util: {util:.4f}",
         f"valu_per_mfma: {valu_other / c['SQ_INSTS_MFMA']:.3f}",
         f"lds_per_mfma: {c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.3f}",
@@ -337,19 +376,21 @@ def summarize_profile(workload: str, prof_dir: str, digest: str | None = None, c
     return "\n".join(lines)
 
 
-def collect_profile(workload: str, out_dir: str) -> str:
+def collect_profile(workload: str, out_dir: str, backward: bool = False) -> dict:
     """Run the counter passes (each rocprofv3 with this program after `--`, under a time limit) and
-    return the summary.  This process itself never touches the GPU."""
+    return {kernel: summary}: the forward's, or with backward=True the two backward kernels'.
+    This process itself never touches the GPU."""
     import subprocess
     env = dict(os.environ, TMPDIR="/tmp")
-    cmds = profile_commands(workload, out_dir)
+    cmds = profile_commands(workload, out_dir, backward=backward)
     for name, argv in cmds:
         print(f"bench.py: counter pass {name} for {workload}", file=sys.stderr, flush=True)
         r = subprocess.run(["timeout", "-s", "KILL", "180", *argv], cwd="/tmp", env=env,
                            stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"counter pass {name} failed ({r.returncode}): {r.stderr[-2000:]}")
-    return summarize_profile(workload, out_dir, commands=cmds)
+    kernels = ("bwd_dq", "bwd_dkdv") if backward else ("fwd",)
+    return {k: summarize_profile(workload, out_dir, commands=cmds, kernel=k) for k in kernels}
 
 
 def flops_per_step(w) -> float:
@@ -773,18 +814,26 @@ def main():
                          "profiles/ (this process starts rocprofv3 runs and touches no GPU itself)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="print the summary of counter passes already in DIR (mfma/, fetch/, write/)")
+    ap.add_argument("--profile-kernel", default="fwd", choices=("fwd", "bwd", "bwd_dq", "bwd_dkdv"),
+                    help="which kernel the counter passes cover: the forward, or the backward (collect: "
+                         "bwd, writing both backward summaries; summarize: bwd_dq or bwd_dkdv)"),
     args = ap.parse_args()
 
     if args.summarize_profile or args.collect_profile:
         from transformer_scaled_dot_03_amd.workloads import HEADLINE
         name = args.workload or HEADLINE
         if args.collect_profile:
-            text = collect_profile(name, os.path.abspath(args.collect_profile))
-            with open(counters_path(name), "w") as f:
-                f.write(text)
+            if args.profile_kernel not in ("fwd", "bwd"):
+                ap.error("--collect-profile takes --profile-kernel fwd or bwd")
+            texts = collect_profile(name, os.path.abspath(args.collect_profile), backward=args.profile_kernel == "bwd")
+            for kern, text in texts.items():
+                with open(counters_path(name, kern), "w") as f:
+                    f.write(text)
+                print(text)
         else:
-            text = summarize_profile(name, args.summarize_profile)
-        print(text)
+            if args.profile_kernel == "bwd":
+                ap.error("--summarize-profile takes --profile-kernel fwd, bwd_dq or bwd_dkdv")
+            print(summarize_profile(name, args.summarize_profile, kernel=args.profile_kernel))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -882,6 +931,13 @@ def main():
     }
     if not args.no_backward and w.dtype == "bf16":
         rec["backward"] = time_backward(torch, tsd, w, qd, kd, vd, kld, args.steps, args.warmup)
+        bd = kernel_source_digest("bwd")
+        for kern in ("bwd_dq", "bwd_dkdv"):
+            cnt = committed_counters(name, bd, kern)
+            rec["backward"][kern] = None if cnt is None else {
+                "mfma_util": cnt.get("mfma_util"), "hbm_bytes_per_launch": cnt.get("hbm_bytes_per_launch"),
+                "kernel_us": cnt.get("kernel_us"), "kernel_source_digest": bd,
+                "counters": "profiles/" + os.path.basename(counters_path(name, kern))}
     if not args.no_decode:
         from transformer_scaled_dot_03_amd.workloads import DECODE_HEADLINE
         rec["decode"] = time_decode(torch, tsd, args.decode_workload or DECODE_HEADLINE, args.steps, args.warmup)

@@ -173,3 +173,89 @@ def test_summary_shows_the_output_directory_as_a_placeholder():
     for sub in ("mfma", "fetch", "write", "trace"):
         assert f"-d <out>/{sub} " in text
     assert "-- python3 bench.py --workload " + FIX_WORKLOAD in text
+
+
+BWD_FIXTURE = os.path.join(ROOT, "tests", "golden", "rocprof_bwd_enc_self_b32h8t256d64")
+
+
+def _rows(fixture, sub, name):
+    import csv
+    with open(os.path.join(fixture, sub, name), newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, counter, name):
+    vals = {}
+    for r in rows:
+        if name in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+@pytest.mark.parametrize("kernel,kname", [("bwd_dq", "attn_bwd_dq_kernel<64, false, true>"),
+                                          ("bwd_dkdv", "attn_bwd_dkdv_kernel<64, false, true>")])
+def test_backward_profile_summary_of_a_recorded_rocprofv3_run(kernel, kname):
+    """tests/golden/rocprof_bwd_enc_self_b32h8t256d64: rocprofv3 CSVs of `bench.py --collect-profile
+    --profile-kernel bwd` on the encoder key-padding workload (attn_fwd_lse, then attn_bwd: the dQ and
+    the dK/dV kernel), trimmed to two dispatches of each kernel per counter pass, the calibration
+    copies and 34 traced launches of each.  Each kernel's summary must reproduce the figures computed
+    here from its own rows only."""
+    sys.path.insert(0, ROOT)
+    import bench
+    text = bench.summarize_profile(FIX_WORKLOAD, BWD_FIXTURE, digest="e" * 16, kernel=kernel)
+    vals = _machine_lines(text)
+    assert vals["kernel"] == kernel and vals["kernel_source_digest"] == "e" * 16
+    assert text.startswith(f"# Counters: attn::{kname} on {FIX_WORKLOAD}")
+    rows = _rows(BWD_FIXTURE, "mfma", "run_counter_collection.csv")
+    busy = _per_dispatch(rows, "SQ_VALU_MFMA_BUSY_CYCLES", kname)
+    grbm = _per_dispatch(rows, "GRBM_GUI_ACTIVE", kname)
+    assert len(busy) == 2 and len(grbm) == 2
+    util = (sum(busy) / 2 / 1024) / (sum(grbm) / 2 / 8)
+    assert abs(float(vals["mfma_util"]) - util) < 1e-4
+
+    def scaled(sub, counter):
+        rs = _rows(BWD_FIXTURE, sub, "run_counter_collection.csv")
+        k = _per_dispatch(rs, counter, kname)
+        grids = {}
+        for r in rs:
+            if "copyBuffer" in r["Kernel_Name"]:
+                grids.setdefault(int(r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        cal = grids[max(grids)]
+        return (sum(k) / len(k)) * (256 * 1024 / (sum(cal) / len(cal))) * 1024
+
+    rd, wr = scaled("fetch", "FETCH_SIZE"), scaled("write", "WRITE_SIZE")
+    assert abs(float(vals["hbm_bytes_per_launch"]) - (rd + wr)) <= 2.0
+    # the dQ kernel writes dQ (bf16) plus two fp32 values per row; the dK/dV kernel dK and dV
+    B, h, T, d = 32, 8, 256, 64
+    want_wr = 2 * B * h * T * d + 8 * B * h * T if kernel == "bwd_dq" else 2 * 2 * B * h * T * d
+    assert abs(wr - want_wr) / want_wr < 0.02
+    durs = [float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            for r in _rows(BWD_FIXTURE, "trace", "run_kernel_trace.csv") if kname in r["Kernel_Name"]]
+    assert len(durs) == 34
+    assert abs(float(vals["kernel_us"]) - sum(durs[30:]) / 4 / 1e3) < 1e-3
+
+
+def test_backward_summaries_are_keyed_to_the_backward_source(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    fwd, bwd = bench.kernel_source_digest("fwd"), bench.kernel_source_digest("bwd")
+    assert fwd != bwd and fwd == bench.kernel_source_digest()
+    for kern in ("bwd_dq", "bwd_dkdv"):
+        with open(bench.counters_path(FIX_WORKLOAD, kern), "w") as f:
+            f.write(bench.summarize_profile(FIX_WORKLOAD, BWD_FIXTURE, kernel=kern))
+        assert os.path.basename(bench.counters_path(FIX_WORKLOAD, kern)).startswith(f"attn_{kern}_")
+        got = bench.committed_counters(FIX_WORKLOAD, bwd, kern)
+        assert got is not None and 0 < got["mfma_util"] < 1 and got["kernel_us"] > 0
+        # figures taken on other code, or asked for under the forward's digest, are not reported
+        assert bench.committed_counters(FIX_WORKLOAD, fwd, kern) is None
+    assert bench.committed_counters(FIX_WORKLOAD, fwd, "fwd") is None   # no forward summary written here
+
+
+def test_backward_profile_runs_keep_the_backward_leg():
+    sys.path.insert(0, ROOT)
+    import bench
+    for name, argv in bench.profile_commands(FIX_WORKLOAD, "/tmp/x", backward=True):
+        assert "--no-backward" not in argv and argv[argv.index("--") + 1] == sys.executable
+    for name, argv in bench.profile_commands(FIX_WORKLOAD, "/tmp/x"):
+        assert "--no-backward" in argv
