@@ -31,7 +31,8 @@ PROBE_SOURCES = ["mfma_probe.hip"]
 # before reading LDS (no load overlaps compute): the race check of the staging
 SERIAL_TEST_LIB_PATH = os.path.join(PKG, "libattn_serial_test.so")
 TARGETS = [(LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)]
-TEST_TARGETS = [(SERIAL_TEST_LIB_PATH, SOURCES, ["-DATTN_FWD_TEST_SERIAL_STAGING=1"])]
+TEST_TARGETS = [(SERIAL_TEST_LIB_PATH, SOURCES, ["-DATTN_FWD_TEST_SERIAL_STAGING=1", "-DATTN_BWD_TEST_SERIAL_STAGING=1",
+                                                 "-DATTN_GEMM_TEST_SERIAL_STAGING=1"])]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code (kept out on

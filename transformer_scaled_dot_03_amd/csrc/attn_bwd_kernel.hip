@@ -33,7 +33,18 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+// A test-only build (-DATTN_BWD_TEST_SERIAL_STAGING=1, built as
+// libattn_serial_test.so, never as libattn.so) waits for each step's
+// direct-to-LDS loads before the step reads LDS, in the dQ, dK/dV and weights
+// kernels: no load is in flight while any wave reads a tile, so the staging
+// cannot race; their outputs must equal the pipelined kernels' bit for bit.
+#ifndef ATTN_BWD_TEST_SERIAL_STAGING
+#define ATTN_BWD_TEST_SERIAL_STAGING 0
+#endif
+
 namespace attn {
+
+constexpr bool kBwdSerialStaging = ATTN_BWD_TEST_SERIAL_STAGING != 0;
 
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
@@ -269,6 +280,7 @@ __global__ __launch_bounds__(64 * DqShape<D>::kWaves, 8 / DqShape<D>::kWaves) vo
       const int it = it0 + u;
       if (it < ntiles) {
         if (it + 1 < ntiles) load_kv((it + 1) * kBT, u ? kb0 : kb1, u ? vb0 : vb1);
+        if constexpr (kBwdSerialStaging) pipeline_barrier<0>();   // test build only
         if (it < ntw) step(it, u ? kb1 : kb0, u ? vb1 : vb0);
         pipeline_barrier<0>();
       }
@@ -531,9 +543,11 @@ __global__ __launch_bounds__(64 * DkdvShape<D>::kWaves, 1) void attn_bwd_dkdv_ke
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
     load_tile((first + it + 1) * kBT, 1);
+    if constexpr (kBwdSerialStaging) pipeline_barrier<0>();   // test build only
     step(first + it, 0);
     pipeline_barrier<0>();
     if (it + 2 < ntiles) load_tile((first + it + 2) * kBT, 0);
+    if constexpr (kBwdSerialStaging) pipeline_barrier<0>();   // test build only
     step(first + it + 1, 1);
     pipeline_barrier<0>();
   }
@@ -682,6 +696,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_weights_kernel(WtsParams 
       const int it = it0 + u;
       if (it < ntiles) {
         if (it + 1 < ntiles) load_k((it + 1) * kBT, u ? kb0 : kb1);
+        if constexpr (kBwdSerialStaging) pipeline_barrier<0>();   // test build only
         step(it, u ? kb1 : kb0);
         if (!CAUSAL && zt < nall) zero_tile();
         pipeline_barrier<0>();

@@ -41,6 +41,15 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+// A test-only build (-DATTN_GEMM_TEST_SERIAL_STAGING=1, built as
+// libattn_serial_test.so, never as libattn.so) waits for every direct-to-LDS
+// load right after issuing it: no load is in flight while a stage is read, so
+// the staging cannot race; its products must equal the pipelined kernel's bit
+// for bit.
+#ifndef ATTN_GEMM_TEST_SERIAL_STAGING
+#define ATTN_GEMM_TEST_SERIAL_STAGING 0
+#endif
+
 namespace attn {
 
 namespace {
@@ -200,9 +209,11 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void attn_gemm_bf16_kernel(Gemm
     int ks = 0;
     for (; ks + 1 < nk; ks += 2) {
       load(cur, ks + 1, ab1, bb1);
+      if constexpr (ATTN_GEMM_TEST_SERIAL_STAGING != 0) pipeline_barrier<0>();   // test build only
       compute(ab0, bb0);
       pipeline_barrier<0>();
       if (ks + 2 < nk) load(cur, ks + 2, ab0, bb0);
+      if constexpr (ATTN_GEMM_TEST_SERIAL_STAGING != 0) pipeline_barrier<0>();   // test build only
       compute(ab1, bb1);
       pipeline_barrier<0>();
     }
@@ -215,6 +226,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void attn_gemm_bf16_kernel(Gemm
       cur = tile_at(t + t_step);
       load(cur, 0, ab0, bb0);
     }
+    if constexpr (ATTN_GEMM_TEST_SERIAL_STAGING != 0) pipeline_barrier<0>();   // test build only
 
     // ---- epilogue: one rounding to bf16, staged through LDS
 #pragma unroll
