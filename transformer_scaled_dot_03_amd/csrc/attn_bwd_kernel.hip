@@ -23,7 +23,10 @@
 // row/key take the streamed operand from LDS as 16-byte fragments read in
 // slot order sigma; products contracting over the streamed index take it
 // transposed with ds_read_b64_tr_b16.  Both read patterns share one tile
-// layout (dual_swz) that is free of bank conflicts for both.
+// layout that is free of bank conflicts for both: an XOR swizzle of the
+// chunks (dual_swz) with per-step offsets in registers, or, in the d = 128
+// dK/dV kernel, padded 288-byte row slots whose per-step offsets are
+// constants on one base (PadTile128).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
