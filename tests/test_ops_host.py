@@ -163,3 +163,52 @@ def test_valid_fake_call_reaches_the_library():
     q, k, v = qkv()
     with pytest.raises(AssertionError, match="library was called"):
         ops.attention(q, k, v, out=FakeDeviceTensor((B, H, T, D), BF))
+
+
+class FakeStream:
+    """A HIP stream stand-in on a given GPU."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.cuda_stream = 0x1234
+
+
+def _all_calls(stream):
+    q, k, v = qkv()
+    dm = 128
+    x = FakeDeviceTensor((B, T, dm), BF)
+    w = FakeDeviceTensor((dm, dm), BF)
+    return {
+        "attention": lambda: ops.attention(q, k, v, out=FakeDeviceTensor((B, H, T, D), BF), stream=stream),
+        "attention_lse": lambda: ops.attention_lse(q, k, v, stream=stream,
+                                                   out=FakeDeviceTensor((B, H, T, D), BF),
+                                                   lse=FakeDeviceTensor((B, H, T), torch.float32)),
+        "attention_weights": lambda: ops.attention_weights(
+            q, k, v, stream=stream, out=FakeDeviceTensor((B, H, T, D), BF),
+            lse=FakeDeviceTensor((B, H, T), torch.float32), weights=FakeDeviceTensor((B, H, T, T), torch.float32)),
+        "attention_backward": lambda: ops.attention_backward(
+            q, k, v, FakeDeviceTensor((B, H, T, D), BF), FakeDeviceTensor((B, H, T, D), BF),
+            FakeDeviceTensor((B, H, T), torch.float32), stream=stream,
+            dq=FakeDeviceTensor((B, H, T, D), BF), dk=FakeDeviceTensor((B, H, T, D), BF),
+            dv=FakeDeviceTensor((B, H, T, D), BF), delta=FakeDeviceTensor((2, B, H, T), torch.float32)),
+        "decode_attention": lambda: ops.decode_attention(
+            FakeDeviceTensor((B, H, 1, D), BF), k, v, stream=stream, out=FakeDeviceTensor((B, H, 1, D), BF),
+            workspace=FakeDeviceTensor((4096,), torch.uint8)),
+        "multi_head_attention": lambda: ops.multi_head_attention(
+            x, w, w, w, w, heads=2, stream=stream, out=FakeDeviceTensor((B, T, dm), BF),
+            workspace=FakeDeviceTensor((4096,), torch.uint8)),
+    }
+
+
+@pytest.mark.parametrize("name", ["attention", "attention_lse", "attention_weights", "attention_backward",
+                                  "decode_attention", "multi_head_attention"])
+def test_stream_of_another_gpu_is_rejected(name):
+    with pytest.raises(ValueError, match="stream is on cuda:1"):
+        _all_calls(FakeStream("cuda:1"))[name]()
+
+
+@pytest.mark.parametrize("name", ["attention", "attention_lse", "attention_weights", "attention_backward",
+                                  "decode_attention", "multi_head_attention"])
+def test_stream_of_the_inputs_gpu_reaches_the_library(name):
+    with pytest.raises(AssertionError, match="library was called"):
+        _all_calls(FakeStream("cuda:0"))[name]()

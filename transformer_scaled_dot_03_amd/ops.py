@@ -78,6 +78,17 @@ def _ptr(t):
     return None if t is None else (t.data_ptr() or None)
 
 
+def _stream_handle(stream, device):
+    """The HIP stream handle to enqueue on: `stream`, or the current stream of
+    `device`.  A stream of another GPU is refused: its kernel would run there on
+    pointers into this device's memory."""
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if torch.device(stream.device) != torch.device(device):
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+    return stream.cuda_stream
+
+
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None,
               causal: bool = False, key_lens: torch.Tensor | None = None,
               out: torch.Tensor | None = None, stream: torch.cuda.Stream | None = None) -> torch.Tensor:
@@ -91,7 +102,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | 
     mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
-    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = _stream_handle(stream, q.device)
     fn = _lib.attn_fwd if q.dtype == torch.bfloat16 else _lib.attn_fwd_f32
     status = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h, Tq, Tk, dk, dv, float(scale), mask, kl_ptr, st)
     if status != _lib.OK:
@@ -109,7 +120,7 @@ def attention_lse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: floa
     mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
-    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = _stream_handle(stream, q.device)
     status = _lib.attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, h, Tq, Tk, dk, dv,
                                float(scale), mask, kl_ptr, st)
     if status != _lib.OK:
@@ -130,7 +141,7 @@ def attention_weights(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: 
     mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(dk)
-    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = _stream_handle(stream, q.device)
     status = _lib.attn_fwd_weights(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(weights), B, h, Tq, Tk,
                                    dk, dv, float(scale), mask, kl_ptr, st)
     if status != _lib.OK:
@@ -165,7 +176,7 @@ def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: t
     mask, kl_ptr = _mask_args(B, causal, key_lens, q.device)
     if scale is None:
         scale = default_scale(d_k)
-    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = _stream_handle(stream, q.device)
     status = _lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(delta),
                            _ptr(dq), _ptr(dk), _ptr(dv), B, h, Tq, Tk, d_k, d_v, float(scale), mask, kl_ptr, st)
     if status != _lib.OK:
@@ -215,7 +226,7 @@ def decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: f
         raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
     if scale is None:
         scale = default_scale(dk)
-    st = (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
+    st = _stream_handle(stream, q.device)
     status = _lib.attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, h, Tk, dk, dv, float(scale), mask, kl_ptr,
                               _ptr(workspace), workspace.numel(), st)
     if status != _lib.OK:
@@ -260,7 +271,7 @@ def multi_head_attention(xq: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor, w
         raise ValueError("workspace must be a contiguous uint8 tensor on xq's device")
     if scale is None:
         scale = default_scale(dm // heads) if heads > 0 and dm % heads == 0 else 1.0
-    st = (stream if stream is not None else torch.cuda.current_stream(xq.device)).cuda_stream
+    st = _stream_handle(stream, xq.device)
     status = _lib.attn_mha_fwd(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(out),
                                B, Tq, Tk, dm, heads, float(scale), mask, kl_ptr, _ptr(workspace),
                                workspace.numel(), st)
