@@ -38,6 +38,10 @@
  * Asynchrony: the work is enqueued on `stream` (0 = the null stream) and the
  * call returns without synchronising.  key_lens is read by the kernel, so its
  * values are never validated on the host; they are clamped to [0, Tk].
+ * Every pointer of a call must be memory of the device `stream` belongs to
+ * (the null stream: the current device); the library does not look the
+ * pointers' device up, so a mismatch is the caller's error (the Python
+ * wrapper checks it).
  *
  * Errors: 0 on success.  Argument errors return a negative ATTN_ERR_* code
  * before any HIP call is made (nothing is launched); a failed launch returns
